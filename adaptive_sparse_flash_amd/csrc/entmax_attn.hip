@@ -1,0 +1,1331 @@
+// Fused alpha-entmax attention for AMD Instinct MI355X (gfx950, CDNA4).
+//
+// Method (AdaSplash pages, cited by title and section):
+//  * "AdaSplash: Adaptive Sparse Flash Attention" (ICML 2025 talk summary),
+//    "Accelerated Alpha-Entmax Transformation": tau is the root of
+//    f(tau) = sum_j [x_j - tau]_+^beta - 1; its derivatives are shifted powers
+//    times constants, so Halley steps are cheap, and a bisection bracket is
+//    kept so that a Halley step leaving the bracket is replaced by a midpoint.
+//  * Same page, "AdaSplash: Fused GPU Kernel for Attention": one workgroup per
+//    query tile, the Q tile stays on chip, K tiles are streamed and the row
+//    sums of f and its derivatives are accumulated; a second pass streams K/V
+//    and accumulates P V.  S and P never reach HBM.
+//  * Same page, "Exploiting Sparsity": all-zero probability tiles are skipped
+//    (their K/V loads and their MFMA work) in the output pass and backward.
+//  * "AdaSplash-2: The Transformer Revolution We Didn't See Coming", "Sparse
+//    Attention Makes Waves": a coarse per-row histogram of scores kept in
+//    on-chip memory initialises tau so that one or two refinements suffice.
+//
+// MI355X design (not the pages' Triton design):
+//  * MFMA v_mfma_f32_32x32x16_bf16 (fp32 inputs: v_mfma_f32_32x32x2_f32).
+//    Scores are computed transposed, S^T = K Q^T: the 32 MFMA output columns
+//    are queries, so every lane owns one query and per-row sums of f, f', f''
+//    and histogram updates stay inside the lane; only lanes l and l^32 share
+//    a row.  The same register tile, converted to bf16, is the B operand of
+//    O^T = V^T P^T (keys permuted consistently in V^T), so P never leaves
+//    registers.
+//  * t = clamp((alpha-1)/sqrt(d) * acc - tau, 0, 1) is one v_fma_f32 with the
+//    clamp modifier: tau >= max(x) - 1 keeps every t <= 1.
+//  * The first sweep only takes row maxima (MFMA-bound); it also records the
+//    maximum score of every (wave, key tile).  Tiles whose maximum cannot
+//    exceed the lower bracket end max(x) - 1 can never hold a nonzero
+//    probability, so the histogram and Halley sweeps visit candidate tiles only.
+//  * The histogram holds integer moments (count, sum y, sum y^2 of
+//    y = x - lo in 2^-24 fixed point) updated with LDS integer atomics, so it is
+//    deterministic and, for alpha in {1.5, 2}, gives f exactly at bin edges.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+#include <float.h>
+
+#include "entmax_attn.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBQ = 32;               // queries per wave = mask row granularity
+constexpr int kWaves = 4;
+constexpr int kBQW = kBQ * kWaves;    // queries per workgroup (forward, dQ)
+constexpr int kBK = 64;               // keys per tile = mask column granularity
+constexpr int kThreads = kWave * kWaves;
+constexpr int kMaskChunk = 1024;      // key tiles of mask staged in LDS at once
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+enum AlphaKind { AK15 = 0, AK20 = 1, AK125 = 2, AKGEN = 3 };
+
+struct Params {
+  int N, n_kt, n_q32, causal;
+  int Np;                 // N rounded up to 64 (row length of transposed copies)
+  float alpha, beta, scale, inv_sqrt_d;
+  int mode, max_iters, flags;
+  float tol;
+  int out_bf16;
+  int kt_cap;             // key tiles with LDS candidate state (0 = pruning off)
+};
+
+// ----------------------------------------------------------- fragments ---
+// A fragment is the 8 consecutive contraction elements one lane feeds to one
+// 32x32 MFMA step of 16 (bf16: one instruction; fp32: eight 32x32x2 steps).
+template <typename E> struct Frag;
+template <> struct Frag<__bf16> { bf16x8 v; };
+template <> struct Frag<float> { f32x4 a, b; };
+
+__device__ __forceinline__ void frag_zero(Frag<__bf16>& f) {
+  f.v = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+__device__ __forceinline__ void frag_zero(Frag<float>& f) {
+  f.a = f32x4{0, 0, 0, 0};
+  f.b = f32x4{0, 0, 0, 0};
+}
+__device__ __forceinline__ void ld8(Frag<__bf16>& f, const __bf16* p) {
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void ld8(Frag<float>& f, const float* p) {
+  f.a = *reinterpret_cast<const f32x4*>(p);
+  f.b = *reinterpret_cast<const f32x4*>(p + 4);
+}
+// two runs of 4 consecutive elements (transposed tiles, permuted key order)
+__device__ __forceinline__ void ld4x2(Frag<__bf16>& f, const __bf16* p0, const __bf16* p1) {
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void ld4x2(Frag<float>& f, const float* p0, const float* p1) {
+  f.a = *reinterpret_cast<const f32x4*>(p0);
+  f.b = *reinterpret_cast<const f32x4*>(p1);
+}
+// accumulator registers r[0..7] -> operand fragment
+__device__ __forceinline__ void from_acc(Frag<__bf16>& f, const f32x16& acc, int base) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.v[j] = (__bf16)acc[base + j];
+}
+__device__ __forceinline__ void from_acc(Frag<float>& f, const f32x16& acc, int base) {
+  f.a = f32x4{acc[base + 0], acc[base + 1], acc[base + 2], acc[base + 3]};
+  f.b = f32x4{acc[base + 4], acc[base + 5], acc[base + 6], acc[base + 7]};
+}
+// hi/lo bf16 pair: x = hi + lo to about 2^-17 relative (hi = bf16(x), lo = bf16(x - hi);
+// x - hi is exact in fp32).  For fp32 fragments lo is unused.
+__device__ __forceinline__ void split_acc(Frag<__bf16>& hi, Frag<__bf16>& lo, const f32x16& acc, int base) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    __bf16 hv = (__bf16)acc[base + j];
+    hi.v[j] = hv;
+    lo.v[j] = (__bf16)(acc[base + j] - (float)hv);
+  }
+}
+__device__ __forceinline__ void split_acc(Frag<float>& hi, Frag<float>&, const f32x16& acc, int base) {
+  from_acc(hi, acc, base);
+}
+template <typename E> constexpr bool kNeedsLo = sizeof(E) == 2;
+
+__device__ __forceinline__ void mma(f32x16& c, const Frag<__bf16>& a, const Frag<__bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x16& c, const Frag<float>& a, const Frag<float>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[0], b.a[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[1], b.a[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[2], b.a[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.a[3], b.a[3], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[0], b.b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[1], b.b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[2], b.b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[3], b.b[3], c, 0, 0, 0);
+}
+
+// Row (M index) held by register i of a 32x32 accumulator in lane-half h;
+// the column (N index) is lane & 31.
+__device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
+
+__device__ __forceinline__ float clamp01(float v) { return __builtin_amdgcn_fmed3f(v, 0.0f, 1.0f); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// ------------------------------------------------------ entmax powers ---
+// t in [0, 1].  p = t^beta, u = t^(beta-1) (0 off the support), and the
+// sweep sums F0 += t^beta, F1 += t^(beta-1), F2 += t^(beta-2), cnt += [t>0].
+template <int AK> struct Ent;
+template <> struct Ent<AK15> {   // beta = 2
+  __device__ static void sweep(float t, float, float& F0, float& F1, float& F2, float& cnt) {
+    F0 = fmaf(t, t, F0);
+    F1 += t;
+    F2 += ceilf(t);
+    (void)cnt;
+  }
+  __device__ static float count(float, float, float F2, float) { return F2; }
+  __device__ static void pu(float t, float, float& p, float& u) { p = t * t; u = t; }
+};
+template <> struct Ent<AK20> {   // beta = 1 (sparsemax)
+  __device__ static void sweep(float t, float, float& F0, float& F1, float&, float&) {
+    F0 += t;
+    F1 += ceilf(t);
+  }
+  __device__ static float count(float, float F1, float, float) { return F1; }
+  __device__ static void pu(float t, float, float& p, float& u) { p = t; u = ceilf(t); }
+};
+template <> struct Ent<AK125> {  // beta = 4
+  __device__ static void sweep(float t, float, float& F0, float& F1, float& F2, float& cnt) {
+    float t2 = t * t;
+    F0 = fmaf(t2, t2, F0);
+    F1 = fmaf(t2, t, F1);
+    F2 += t2;
+    cnt += ceilf(t);
+  }
+  __device__ static float count(float, float, float, float cnt) { return cnt; }
+  __device__ static void pu(float t, float, float& p, float& u) {
+    float t2 = t * t;
+    p = t2 * t2;
+    u = t2 * t;
+  }
+};
+template <> struct Ent<AKGEN> {  // any 1 < alpha < 2
+  __device__ static void sweep(float t, float beta, float& F0, float& F1, float& F2, float& cnt) {
+    float l = log2f(t);
+    bool pos = t > 0.0f;
+    F0 += exp2f(beta * l);
+    F1 += pos ? exp2f((beta - 1.0f) * l) : 0.0f;
+    F2 += pos ? exp2f((beta - 2.0f) * l) : 0.0f;
+    cnt += ceilf(t);
+  }
+  __device__ static float count(float, float, float, float cnt) { return cnt; }
+  __device__ static void pu(float t, float beta, float& p, float& u) {
+    float l = log2f(t);
+    p = exp2f(beta * l);
+    u = t > 0.0f ? exp2f((beta - 1.0f) * l) : 0.0f;
+  }
+};
+
+// ------------------------------------------------------- tile staging ---
+// Copy `rows` rows of D elements (global rows row0.., zero past N) into LDS
+// rows of `lstride` bytes, in 16-byte pieces spread over the workgroup.
+template <typename E, int D>
+__device__ __forceinline__ void stage_rows(char* lds, int lstride, const E* g, int row0, int rows,
+                                           int N) {
+  constexpr int CH = D * (int)sizeof(E) / 16;
+  for (int c = threadIdx.x; c < rows * CH; c += kThreads) {
+    int r = c / CH, cc = c - r * CH;
+    int gr = row0 + r;
+    f32x4 val = f32x4{0, 0, 0, 0};
+    if (gr < N)
+      val = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(g + (size_t)gr * D) + cc * 16);
+    *reinterpret_cast<f32x4*>(lds + r * lstride + cc * 16) = val;
+  }
+}
+// Copy columns col0..col0+W of a transposed [D][Np] matrix into LDS [D][W].
+template <typename E, int D, int W>
+__device__ __forceinline__ void stage_cols(char* lds, int lstride, const E* gt, int Np, int col0) {
+  constexpr int CH = W * (int)sizeof(E) / 16;
+  for (int c = threadIdx.x; c < D * CH; c += kThreads) {
+    int r = c / CH, cc = c - r * CH;
+    f32x4 val = *reinterpret_cast<const f32x4*>(
+        reinterpret_cast<const char*>(gt + (size_t)r * Np + col0) + cc * 16);
+    *reinterpret_cast<f32x4*>(lds + r * lstride + cc * 16) = val;
+  }
+}
+
+// S^T for one wave: 64 keys (LDS rows, stride ks) x the wave's 32 queries
+// (B fragments in registers).  acc[kb] holds keys 32kb.. as rows.
+template <typename E, int D>
+__device__ __forceinline__ void scores_T(f32x16 (&acc)[2], const char* klds, int ks,
+                                         const Frag<E> (&qf)[D / 16], int lane) {
+  const int c32 = lane & 31, h = lane >> 5;
+  acc[0] = f32x16{};
+  acc[1] = f32x16{};
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<E> a;
+      ld8(a, reinterpret_cast<const E*>(klds + (32 * kb + c32) * ks) + 16 * c + 8 * h);
+      mma(acc[kb], a, qf[c]);
+    }
+  }
+}
+
+// Mask invisible entries of an S^T tile (rows = keys key0.., column = query iq).
+__device__ __forceinline__ void mask_T(f32x16 (&acc)[2], int key0, int iq, int N, int causal,
+                                       int h) {
+  const bool qok = iq < N;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int j = key0 + 32 * kb + acc_row(i, h);
+      if (!qok || j >= N || (causal && j > iq)) acc[kb][i] = -INFINITY;
+    }
+}
+
+template <typename E, int D>
+__device__ __forceinline__ void load_qfrags(Frag<E> (&qf)[D / 16], const E* rowp, bool valid, int h) {
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    if (valid)
+      ld8(qf[c], rowp + 16 * c + 8 * h);
+    else
+      frag_zero(qf[c]);
+  }
+}
+
+__device__ __forceinline__ int qtile_of_block(const Params& P) {
+  // causal: heaviest query tiles first
+  return P.causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+}
+
+// ------------------------------------------------------------- k_tau ---
+// Per workgroup (128 queries): row maxima, optional histogram, Halley /
+// bisection sweeps, tau and the block mask.  Dynamic LDS layout:
+//   K tile [64][D] | histogram [128][BINS][2] u64 | tile max [4][cap] f32 |
+//   candidate [4][cap] u8 | candidate list [cap] i16 | counters
+template <typename E, int D, int AK, int BINS>
+__global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
+                                                  Params P, float* __restrict__ tau_out,
+                                                  uint8_t* __restrict__ mask_out,
+                                                  uint8_t* __restrict__ iters_out) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int KS = D * (int)sizeof(E) + 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
+  const int bh = blockIdx.y;
+  const int qtile = qtile_of_block(P);
+  const int N = P.N;
+  const int q0 = qtile * kBQW;
+  const int wq0 = q0 + kBQ * w;
+  const int iq = wq0 + c32;
+  const bool valid = iq < N;
+  const bool wave_rows = wq0 < N;
+  const E* Qh = Q + (size_t)bh * N * D;
+  const E* Kh = K + (size_t)bh * N * D;
+  const int cap = P.kt_cap;
+  const bool dense = (P.flags & EA_FLAG_FORCE_DENSE) != 0;
+  const bool prune = cap > 0 && P.n_kt <= cap && !dense;
+
+  char* ktile = smem;
+  unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem + kBK * KS);
+  float* tmx = reinterpret_cast<float*>(hist + kBQW * BINS * 2);
+  uint8_t* cand = reinterpret_cast<uint8_t*>(tmx + kWaves * cap);
+  short* list = reinterpret_cast<short*>(cand + kWaves * cap);
+  int* counters = reinterpret_cast<int*>(list + cap + (cap & 1));
+
+  Frag<E> qf[D / 16];
+  load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
+
+  const int wq_last = min(N - 1, wq0 + kBQ - 1);
+  const int kt_end_w = !wave_rows ? 0 : (P.causal ? wq_last / kBK + 1 : P.n_kt);
+  const int wg_last = min(N - 1, q0 + kBQW - 1);
+  const int kt_end = P.causal ? wg_last / kBK + 1 : P.n_kt;
+  const bool wave_has_tail = wq0 + kBQ > N;
+
+  // ---- sweep 0: row maxima (and per-(wave, tile) maxima for pruning)
+  float m = -INFINITY;
+  for (int kt = 0; kt < kt_end; ++kt) {
+    __syncthreads();
+    stage_rows<E, D>(ktile, KS, Kh, kt * kBK, kBK, N);
+    __syncthreads();
+    if (kt < kt_end_w) {
+      f32x16 acc[2];
+      scores_T<E, D>(acc, ktile, KS, qf, lane);
+      const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
+      if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
+      float tm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tm = fmaxf(tm, fmaxf(acc[0][i], acc[1][i]));
+      m = fmaxf(m, tm);
+      if (prune) {
+        float wm = wave_max(tm);
+        if (lane == 0) tmx[w * cap + kt] = wm;
+      }
+    } else if (prune && lane == 0 && w < kWaves) {
+      tmx[w * cap + kt] = -INFINITY;
+    }
+  }
+  m = fmaxf(m, __shfl_xor(m, 32));
+
+  // ---- provable bracket [lo, hi]:  f(max x - 1) >= 0 >= f(max x - n^(1-alpha))
+  const float xmax = m * P.scale;
+  float lo = 0.0f, hi = 0.0f, tau = 0.0f;
+  if (valid) {
+    double dl = (double)xmax - 1.0;
+    lo = (float)dl;
+    if ((double)lo > dl) lo = nextafterf(lo, -INFINITY);
+    double n = P.causal ? (double)(iq + 1) : (double)N;
+    double dh = (double)xmax - pow(n, 1.0 - (double)P.alpha);
+    hi = (float)dh;
+    if ((double)hi < dh) hi = nextafterf(hi, INFINITY);
+    if (hi < lo) hi = lo;
+  }
+  bool conv = !valid;
+  int iters = 0;
+
+  // ---- candidate tiles: some score of the tile can exceed the wave's lowest lo
+  const float lo_w = wave_min(valid ? lo : INFINITY);
+  if (prune) {
+    for (int kt = lane; kt < kt_end; kt += kWave) {
+      bool c = kt < kt_end_w && tmx[w * cap + kt] * P.scale >= lo_w;
+      cand[w * cap + kt] = c ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (prune && w == 0) {
+    int count = 0;
+    for (int base = 0; base < kt_end; base += kWave) {
+      int kt = base + lane;
+      bool bit = false;
+      if (kt < kt_end)
+        bit = cand[kt] | cand[cap + kt] | cand[2 * cap + kt] | cand[3 * cap + kt];
+      unsigned long long bal = __ballot(bit);
+      int before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (bit) list[count + before] = (short)kt;
+      count += __popcll(bal);
+    }
+    if (lane == 0) counters[0] = count;
+  }
+  __syncthreads();
+  const int n_visit = prune ? counters[0] : kt_end;
+
+  // ---- histogram initialisation (AdaSplash-2)
+  if (P.mode == EA_TAU_HIST_HALLEY) {
+    for (int e = threadIdx.x; e < kBQW * BINS * 2; e += kThreads) hist[e] = 0ull;
+    constexpr int SHIFT = 24 - (BINS == 16 ? 4 : 3);
+    for (int idx = 0; idx < n_visit; ++idx) {
+      const int kt = prune ? list[idx] : idx;
+      __syncthreads();
+      stage_rows<E, D>(ktile, KS, Kh, kt * kBK, kBK, N);
+      __syncthreads();
+      const bool wc = prune ? cand[w * cap + kt] != 0 : kt < kt_end_w;
+      if (wc) {
+        f32x16 acc[2];
+        scores_T<E, D>(acc, ktile, KS, qf, lane);
+        const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
+        if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
+        unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * BINS * 2;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float y = fmaf(acc[kb][i], P.scale, -lo);
+            if (y > 0.0f) {
+              unsigned Y = (unsigned)(y * 16777216.0f);
+              int b = min((int)(Y >> SHIFT), BINS - 1);
+              atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
+              atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
+            }
+          }
+      }
+    }
+    __syncthreads();
+    if (valid) {
+      const unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * BINS * 2;
+      const double inv24 = 1.0 / 16777216.0, inv48 = inv24 * inv24;
+      const double beta = (double)P.beta;
+      const bool exact = (AK == AK15 || AK == AK20);
+      double C = 0, S1 = 0, S2 = 0;       // moments of bins above the current edge
+      double f_hi = -1.0;                  // f at the upper edge of the bin under test
+      int bstar = 0;
+      double f_lo = 0, cstar = 0, Cs = 0, S1s = 0, S2s = 0;
+      for (int b = BINS - 1; b >= 0; --b) {
+        unsigned long long h1 = hr[2 * b], h2 = hr[2 * b + 1];
+        double cb = (double)(h1 >> 40);
+        double s1 = (double)(h1 & ((1ull << 40) - 1ull)) * inv24;
+        double s2 = (double)h2 * inv48;
+        double e = (double)b / BINS;
+        double Cn = C + cb, S1n = S1 + s1, S2n = S2 + s2;
+        double f;
+        if (AK == AK15) {
+          f = S2n - 2.0 * e * S1n + e * e * Cn - 1.0;
+        } else if (AK == AK20) {
+          f = S1n - e * Cn - 1.0;
+        } else {
+          // general alpha: each bin's elements stand at their mean (estimate only)
+          f = -1.0;
+          for (int bb = b; bb < BINS; ++bb) {
+            unsigned long long g1 = hr[2 * bb];
+            double cc = (double)(g1 >> 40);
+            if (cc > 0) {
+              double mean = (double)(g1 & ((1ull << 40) - 1ull)) * inv24 / cc;
+              f += cc * pow(fmax(mean - e, 0.0), beta);
+            }
+          }
+        }
+        if (f >= 0.0 || b == 0) {
+          bstar = b;
+          f_lo = f;
+          cstar = cb;
+          Cs = C;
+          S1s = S1;
+          S2s = S2;
+          break;
+        }
+        f_hi = f;
+        C = Cn;
+        S1 = S1n;
+        S2 = S2n;
+      }
+      const double eb = (double)bstar / BINS, eb1 = (double)(bstar + 1) / BINS;
+      double t0 = -1.0;
+      if (exact && cstar == 0.0 && Cs > 0.0) {
+        if (AK == AK15) {
+          double disc = S1s * S1s - Cs * (S2s - 1.0);
+          if (disc >= 0.0) t0 = (S1s - sqrt(disc)) / Cs;
+        } else {
+          t0 = (S1s - 1.0) / Cs;
+        }
+        if (!(t0 >= eb && t0 <= eb1)) t0 = -1.0;
+      }
+      if (t0 < 0.0) {
+        double den = f_lo - f_hi;
+        t0 = den > 0.0 ? eb + (eb1 - eb) * (f_lo / den) : 0.5 * (eb + eb1);
+      }
+      float t0x = (float)((double)lo + t0);
+      if (exact) {
+        const float margin = fmaxf(1.0f, fabsf(xmax)) * 5e-7f + 1e-6f;
+        float nlo = (float)((double)lo + eb) - margin;
+        float nhi = (float)((double)lo + eb1) + margin;
+        if (nlo > lo) lo = nlo;
+        if (nhi < hi) hi = nhi;
+      }
+      tau = fminf(fmaxf(t0x, lo), hi);
+    }
+  } else if (P.mode == EA_TAU_HALLEY_BISECT) {
+    tau = lo;
+  } else {
+    tau = 0.5f * (lo + hi);
+  }
+
+  // ---- refinement sweeps (Halley-bisection or bisection)
+  uint8_t* mrow = mask_out + ((size_t)bh * P.n_q32 + (size_t)(qtile * kWaves + w)) * P.n_kt;
+  if (wave_rows) {
+    for (int kt = lane; kt < P.n_kt; kt += kWave) mrow[kt] = (dense && kt < kt_end_w) ? 1 : 0;
+  }
+  const double beta = (double)P.beta;
+  const int max_iters = P.max_iters;
+  for (int sweep = 0; sweep <= max_iters + 1; ++sweep) {
+    const bool wave_busy = __ballot(!conv) != 0ull;
+    if (!__syncthreads_or(wave_busy ? 1 : 0)) break;
+    float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
+    for (int idx = 0; idx < n_visit; ++idx) {
+      const int kt = prune ? list[idx] : idx;
+      __syncthreads();
+      stage_rows<E, D>(ktile, KS, Kh, kt * kBK, kBK, N);
+      __syncthreads();
+      const bool wc = prune ? cand[w * cap + kt] != 0 : kt < kt_end_w;
+      if (wave_busy && wc) {
+        f32x16 acc[2];
+        scores_T<E, D>(acc, ktile, KS, qf, lane);
+        const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
+        if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
+        const float before = Ent<AK>::count(F0, F1, F2, cnt);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float t = clamp01(fmaf(acc[kb][i], P.scale, -tau));
+            Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
+          }
+        if (!dense) {
+          const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
+          if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
+        }
+      }
+    }
+    F0 += __shfl_xor(F0, 32);
+    F1 += __shfl_xor(F1, 32);
+    F2 += __shfl_xor(F2, 32);
+    if (!conv) {
+      ++iters;
+      const double f = (double)F0 - 1.0;
+      // tau is a float: one ulp of tau moves f by about |f'| ulp, so |f| below
+      // that granularity (or a Halley step below two ulps) is machine precision.
+      const double ulp = (double)FLT_EPSILON * fmax(1.0, fabs((double)tau));
+      const double fp = -beta * (double)F1;
+      const bool bisect = P.mode == EA_TAU_BISECT;
+      if (fabs(f) <= (double)P.tol + (bisect ? 0.0 : 2.0 * fabs(fp) * ulp)) {
+        conv = true;
+      } else {
+        if (f > 0.0) lo = tau; else hi = tau;
+        const float wtol = bisect ? 1e-6f * fmaxf(1.0f, fabsf(tau)) : 4.0f * (float)ulp;
+        if (hi - lo <= wtol || iters >= max_iters) {
+          conv = true;
+        } else {
+          double next = 0.5 * ((double)lo + (double)hi);
+          if (!bisect) {
+            const double fpp = (AK == AK20) ? 0.0 : beta * (beta - 1.0) * (double)F2;
+            const double den = 2.0 * fp * fp - f * fpp;
+            const double th = (double)tau - 2.0 * f * fp / den;
+            if (fabs(th - (double)tau) <= 2.0 * ulp) {
+              conv = true;                        // converged: keep the evaluated tau
+            } else if (th > (double)lo && th < (double)hi) {
+              next = th;
+            }
+          }
+          if (!conv) {
+            float nt = (float)next;
+            if (!(nt > lo && nt < hi)) nt = lo + 0.5f * (hi - lo);
+            if (!(nt > lo && nt < hi)) conv = true;   // bracket exhausted in float
+            else tau = nt;
+          }
+        }
+      }
+    }
+  }
+
+  if (valid && h == 0) {
+    tau_out[(size_t)bh * N + iq] = tau;
+    if (iters_out) iters_out[(size_t)bh * N + iq] = (uint8_t)min(iters, 255);
+  }
+}
+
+// -------------------------------------------------------------- k_pv ---
+// Per workgroup (128 queries): O = P V and W = (U V) / sum(U) over the
+// active key tiles of the block mask.  U = t^(beta-1) is the entmax
+// Jacobian weight; W carries delta_i = dO_i . W_i to the backward.
+template <typename E, int D, int AK>
+__global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const E* __restrict__ K,
+                                                 const E* __restrict__ Vt,
+                                                 const float* __restrict__ tau_in,
+                                                 const uint8_t* __restrict__ mask, Params P,
+                                                 void* __restrict__ out, float* __restrict__ aux) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr int VS = kBK * (int)sizeof(E) + 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
+  const int bh = blockIdx.y;
+  const int qtile = qtile_of_block(P);
+  const int N = P.N;
+  const int wq0 = qtile * kBQW + kBQ * w;
+  const int iq = wq0 + c32;
+  const bool valid = iq < N;
+  const bool wave_rows = wq0 < N;
+  const E* Qh = Q + (size_t)bh * N * D;
+  const E* Kh = K + (size_t)bh * N * D;
+  const E* Vth = Vt + (size_t)bh * D * P.Np;
+
+  char* ktile = smem;
+  char* vtile = smem + kBK * KS;
+  uint8_t* mstage = reinterpret_cast<uint8_t*>(vtile + D * VS);   // [4][kMaskChunk]
+
+  Frag<E> qf[D / 16];
+  load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
+  const float tau = valid ? tau_in[(size_t)bh * N + iq] : INFINITY;
+  const bool wave_has_tail = wq0 + kBQ > N;
+  const bool want_aux = aux != nullptr;
+
+  f32x16 oacc[D / 32], uacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    oacc[db] = f32x16{};
+    uacc[db] = f32x16{};
+  }
+  float usum = 0.0f;
+
+  const int row0 = qtile * kWaves;
+  for (int base = 0; base < P.n_kt; base += kMaskChunk) {
+    const int nk = min(kMaskChunk, P.n_kt - base);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kWaves * kMaskChunk; e += kThreads) {
+      int ww = e / kMaskChunk, kk = e - ww * kMaskChunk;
+      uint8_t b = 0;
+      if (kk < nk && row0 + ww < P.n_q32) b = mask[((size_t)bh * P.n_q32 + row0 + ww) * P.n_kt + base + kk];
+      mstage[e] = b;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < nk; ++kk) {
+      const bool any = (mstage[kk] | mstage[kMaskChunk + kk] | mstage[2 * kMaskChunk + kk] |
+                        mstage[3 * kMaskChunk + kk]) != 0;
+      if (!any) continue;
+      const int kt = base + kk;
+      __syncthreads();
+      stage_rows<E, D>(ktile, KS, Kh, kt * kBK, kBK, N);
+      stage_cols<E, D, kBK>(vtile, VS, Vth, P.Np, kt * kBK);
+      __syncthreads();
+      if (wave_rows && mstage[w * kMaskChunk + kk]) {
+        f32x16 acc[2];
+        scores_T<E, D>(acc, ktile, KS, qf, lane);
+        const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
+        if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
+        f32x16 uu[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float t = clamp01(fmaf(acc[kb][i], P.scale, -tau));
+            float p, u;
+            Ent<AK>::pu(t, P.beta, p, u);
+            acc[kb][i] = p;
+            uu[kb][i] = u;
+            usum += u;
+          }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            Frag<E> pf, uf, ul;
+            from_acc(pf, acc[kb], 8 * s);
+            // U V feeds delta = dO . (U V) / sum(U) in the backward, where it is
+            // subtracted from dP: keep U to ~2^-17 with a hi/lo pair.
+            split_acc(uf, ul, uu[kb], 8 * s);
+            const int koff = 32 * kb + 16 * s + 4 * h;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+              const E* vrow = reinterpret_cast<const E*>(vtile + (32 * db + c32) * VS);
+              Frag<E> vf;
+              ld4x2(vf, vrow + koff, vrow + koff + 8);
+              mma(oacc[db], vf, pf);
+              if (want_aux) {
+                mma(uacc[db], vf, uf);
+                if constexpr (kNeedsLo<E>) mma(uacc[db], vf, ul);
+              }
+            }
+          }
+      }
+    }
+  }
+  usum += __shfl_xor(usum, 32);
+  if (!valid) return;
+  const float inv_u = usum > 0.0f ? 1.0f / usum : 0.0f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * db + 8 * g + 4 * h;
+      const size_t off = ((size_t)bh * N + iq) * D + d0;
+      f32x4 o = f32x4{oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+      if (P.out_bf16) {
+        bf16x4 ob = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + off) = ob;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = o;
+      }
+      if (aux) {
+        f32x4 a = f32x4{uacc[db][4 * g] * inv_u, uacc[db][4 * g + 1] * inv_u,
+                        uacc[db][4 * g + 2] * inv_u, uacc[db][4 * g + 3] * inv_u};
+        *reinterpret_cast<f32x4*>(aux + off) = a;
+      }
+    }
+}
+
+// --------------------------------------------------------- transposes ---
+// [BH][N][D] -> [BH][D][Np], zero for n in [N, Np).
+template <typename E>
+__global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ in, E* __restrict__ outp,
+                                                   int N, int D, int Np) {
+  __shared__ E t[64][65];
+  const E* src = in + (size_t)blockIdx.z * N * D;
+  E* dst = outp + (size_t)blockIdx.z * D * Np;
+  const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    int r = e >> 6, c = e & 63;
+    int n = n0 + r;
+    t[r][c] = n < N ? src[(size_t)n * D + d0 + c] : (E)0.0f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    int r = e >> 6, c = e & 63;
+    dst[(size_t)(d0 + r) * Np + n0 + c] = t[c][r];
+  }
+}
+
+// delta_i = dO_i . W_i, one wave per row.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_delta(const E* __restrict__ dO, const float* __restrict__ W,
+                                               float* __restrict__ delta, long long rows) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float s = 0.0f;
+#pragma unroll
+  for (int d = lane; d < D; d += 64) s = fmaf((float)dO[row * D + d], W[row * D + d], s);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) delta[row] = s;
+}
+
+// ---------------------------------------------------------- k_bwd_dq ---
+// Per workgroup (128 queries): dQ = dS K / sqrt(d) over active key tiles,
+// dS^T = U (dP^T - delta) with dP^T = V dO^T, all in the S^T layout.
+template <typename E, int D, int AK>
+__global__ __launch_bounds__(kThreads) void k_bwd_dq(
+    const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+    const E* __restrict__ dO, const E* __restrict__ Kt, const float* __restrict__ tau_in,
+    const float* __restrict__ delta_in, const uint8_t* __restrict__ mask, Params P,
+    void* __restrict__ dq) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr int VS = kBK * (int)sizeof(E) + 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
+  const int bh = blockIdx.y;
+  const int qtile = qtile_of_block(P);
+  const int N = P.N;
+  const int wq0 = qtile * kBQW + kBQ * w;
+  const int iq = wq0 + c32;
+  const bool valid = iq < N;
+  const bool wave_rows = wq0 < N;
+  const size_t hoff = (size_t)bh * N * D;
+
+  char* ktile = smem;
+  char* vtile = smem + kBK * KS;
+  char* kttile = vtile + kBK * KS;
+  uint8_t* mstage = reinterpret_cast<uint8_t*>(kttile + D * VS);
+
+  Frag<E> qf[D / 16], of[D / 16];
+  load_qfrags<E, D>(qf, Q + hoff + (size_t)iq * D, valid, h);
+  load_qfrags<E, D>(of, dO + hoff + (size_t)iq * D, valid, h);
+  const float tau = valid ? tau_in[(size_t)bh * N + iq] : INFINITY;
+  const float dlt = valid ? delta_in[(size_t)bh * N + iq] : 0.0f;
+  const bool wave_has_tail = wq0 + kBQ > N;
+
+  f32x16 gacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) gacc[db] = f32x16{};
+
+  const int row0 = qtile * kWaves;
+  for (int base = 0; base < P.n_kt; base += kMaskChunk) {
+    const int nk = min(kMaskChunk, P.n_kt - base);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kWaves * kMaskChunk; e += kThreads) {
+      int ww = e / kMaskChunk, kk = e - ww * kMaskChunk;
+      uint8_t b = 0;
+      if (kk < nk && row0 + ww < P.n_q32) b = mask[((size_t)bh * P.n_q32 + row0 + ww) * P.n_kt + base + kk];
+      mstage[e] = b;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < nk; ++kk) {
+      const bool any = (mstage[kk] | mstage[kMaskChunk + kk] | mstage[2 * kMaskChunk + kk] |
+                        mstage[3 * kMaskChunk + kk]) != 0;
+      if (!any) continue;
+      const int kt = base + kk;
+      __syncthreads();
+      stage_rows<E, D>(ktile, KS, K + hoff, kt * kBK, kBK, N);
+      stage_rows<E, D>(vtile, KS, V + hoff, kt * kBK, kBK, N);
+      stage_cols<E, D, kBK>(kttile, VS, Kt + (size_t)bh * D * P.Np, P.Np, kt * kBK);
+      __syncthreads();
+      if (wave_rows && mstage[w * kMaskChunk + kk]) {
+        f32x16 sacc[2], pacc[2];
+        scores_T<E, D>(sacc, ktile, KS, qf, lane);
+        scores_T<E, D>(pacc, vtile, KS, of, lane);
+        const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
+        if (need) mask_T(sacc, kt * kBK, iq, N, P.causal, h);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float t = clamp01(fmaf(sacc[kb][i], P.scale, -tau));
+            float p, u;
+            Ent<AK>::pu(t, P.beta, p, u);
+            sacc[kb][i] = u * (pacc[kb][i] - dlt);
+          }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            // dQ = sum_j dS_ij k_j cancels strongly when the supporting keys are
+            // nearly parallel (sum_j dS_ij = 0): dS goes in as a hi/lo bf16 pair.
+            Frag<E> sf, sl;
+            split_acc(sf, sl, sacc[kb], 8 * s);
+            const int koff = 32 * kb + 16 * s + 4 * h;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+              const E* krow = reinterpret_cast<const E*>(kttile + (32 * db + c32) * VS);
+              Frag<E> kf;
+              ld4x2(kf, krow + koff, krow + koff + 8);
+              mma(gacc[db], kf, sf);
+              if constexpr (kNeedsLo<E>) mma(gacc[db], kf, sl);
+            }
+          }
+      }
+    }
+  }
+  if (!valid) return;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * db + 8 * g + 4 * h;
+      const size_t off = hoff + (size_t)iq * D + d0;
+      f32x4 o = f32x4{gacc[db][4 * g], gacc[db][4 * g + 1], gacc[db][4 * g + 2], gacc[db][4 * g + 3]} *
+                P.inv_sqrt_d;
+      if (P.out_bf16) {
+        bf16x4 ob = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(dq) + off) = ob;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off) = o;
+      }
+    }
+}
+
+// -------------------------------------------------------- k_bwd_dkdv ---
+// Per workgroup (128 keys, 32 per wave): dV = P^T dO and dK = dS^T Q / sqrt(d)
+// over the active 32-query blocks of the two mask columns it covers.  Scores
+// are computed as S = Q K^T here (lane = key), so P and dS feed the A operand
+// and the transposed Q / dO tiles the B operand.
+template <typename E, int D, int AK>
+__global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
+    const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+    const E* __restrict__ dO, const E* __restrict__ Qt, const E* __restrict__ dOt,
+    const float* __restrict__ tau_in, const float* __restrict__ delta_in,
+    const uint8_t* __restrict__ mask, Params P, void* __restrict__ dk, void* __restrict__ dv) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr int TS = kBQ * (int)sizeof(E) + 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
+  const int bh = blockIdx.y;
+  const int ktile = blockIdx.x;
+  const int N = P.N;
+  const int kw0 = ktile * 128 + 32 * w;
+  const int jk = kw0 + c32;
+  const bool kvalid = jk < N;
+  const bool wave_keys = kw0 < N;
+  const int kt64 = (ktile * 128) / kBK + (w >> 1);
+  const size_t hoff = (size_t)bh * N * D;
+
+  char* qtl = smem;
+  char* otl = qtl + kBQ * KS;
+  char* qttl = otl + kBQ * KS;
+  char* ottl = qttl + D * TS;
+  float* taus = reinterpret_cast<float*>(ottl + D * TS);
+  float* dels = taus + kBQ;
+  short* list = reinterpret_cast<short*>(dels + kBQ);   // [kMaskChunk]
+  int* counters = reinterpret_cast<int*>(list + kMaskChunk);
+
+  Frag<E> kf[D / 16], vf[D / 16];
+  load_qfrags<E, D>(kf, K + hoff + (size_t)jk * D, kvalid, h);
+  load_qfrags<E, D>(vf, V + hoff + (size_t)jk * D, kvalid, h);
+
+  f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dka[db] = f32x16{};
+    dva[db] = f32x16{};
+  }
+  const int ktA = (ktile * 128) / kBK, ktB = ktA + 1;
+  const bool hasB = ktB < P.n_kt;
+
+  for (int rbase = 0; rbase < P.n_q32; rbase += kMaskChunk) {
+    const int nr = min(kMaskChunk, P.n_q32 - rbase);
+    __syncthreads();
+    if (w == 0) {
+      int count = 0;
+      for (int b0 = 0; b0 < nr; b0 += kWave) {
+        int r = rbase + b0 + lane;
+        bool bit = false;
+        if (b0 + lane < nr) {
+          const uint8_t* mr = mask + ((size_t)bh * P.n_q32 + r) * P.n_kt;
+          bit = mr[ktA] != 0 || (hasB && mr[ktB] != 0);
+        }
+        unsigned long long bal = __ballot(bit);
+        int before = __popcll(bal & ((1ull << lane) - 1ull));
+        if (bit) list[count + before] = (short)(b0 + lane);
+        count += __popcll(bal);
+      }
+      if (lane == 0) counters[0] = count;
+    }
+    __syncthreads();
+    const int nact = counters[0];
+    for (int ia = 0; ia < nact; ++ia) {
+      const int r = rbase + list[ia];
+      const int qb0 = r * kBQ;
+      __syncthreads();
+      stage_rows<E, D>(qtl, KS, Q + hoff, qb0, kBQ, N);
+      stage_rows<E, D>(otl, KS, dO + hoff, qb0, kBQ, N);
+      stage_cols<E, D, kBQ>(qttl, TS, Qt + (size_t)bh * D * P.Np, P.Np, qb0);
+      stage_cols<E, D, kBQ>(ottl, TS, dOt + (size_t)bh * D * P.Np, P.Np, qb0);
+      if (threadIdx.x < kBQ) {
+        int qi = qb0 + threadIdx.x;
+        taus[threadIdx.x] = qi < N ? tau_in[(size_t)bh * N + qi] : INFINITY;
+        dels[threadIdx.x] = qi < N ? delta_in[(size_t)bh * N + qi] : 0.0f;
+      }
+      __syncthreads();
+      if (!wave_keys) continue;
+      if (mask[((size_t)bh * P.n_q32 + r) * P.n_kt + kt64] == 0) continue;
+      // S = Q K^T and dP = dO V^T: rows = the 32 queries, column = this lane's key
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        Frag<E> a, b;
+        ld8(a, reinterpret_cast<const E*>(qtl + c32 * KS) + 16 * c + 8 * h);
+        mma(sacc, a, kf[c]);
+        ld8(b, reinterpret_cast<const E*>(otl + c32 * KS) + 16 * c + 8 * h);
+        mma(pacc, b, vf[c]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qr = acc_row(i, h);
+        const int qi = qb0 + qr;
+        float s = sacc[i];
+        if (!kvalid || qi >= N || (P.causal && jk > qi)) s = -INFINITY;
+        float t = clamp01(fmaf(s, P.scale, -taus[qr]));
+        float p, u;
+        Ent<AK>::pu(t, P.beta, p, u);
+        sacc[i] = p;
+        pacc[i] = u * (pacc[i] - dels[qr]);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        Frag<E> pf, sf;
+        from_acc(pf, sacc, 8 * s);
+        from_acc(sf, pacc, 8 * s);
+        const int qoff = 16 * s + 4 * h;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const E* orow = reinterpret_cast<const E*>(ottl + (32 * db + c32) * TS);
+          const E* qrow = reinterpret_cast<const E*>(qttl + (32 * db + c32) * TS);
+          Frag<E> ob, qb;
+          ld4x2(ob, orow + qoff, orow + qoff + 8);
+          ld4x2(qb, qrow + qoff, qrow + qoff + 8);
+          mma(dva[db], pf, ob);
+          mma(dka[db], sf, qb);
+        }
+      }
+    }
+  }
+  if (!wave_keys) return;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = kw0 + acc_row(i, h);
+      if (j >= N) continue;
+      const size_t off = hoff + (size_t)j * D + 32 * db + c32;
+      const float vv = dva[db][i], kk = dka[db][i] * P.inv_sqrt_d;
+      if (P.out_bf16) {
+        reinterpret_cast<__bf16*>(dv)[off] = (__bf16)vv;
+        reinterpret_cast<__bf16*>(dk)[off] = (__bf16)kk;
+      } else {
+        reinterpret_cast<float*>(dv)[off] = vv;
+        reinterpret_cast<float*>(dk)[off] = kk;
+      }
+    }
+}
+
+// =============================================================== host ===
+
+struct Shape {
+  int B, H, N, d, esz, n_kt, n_q32, n_qt128, n_kt128, Np;
+  long long BH;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_desc(const ea_desc* desc, Shape* s) {
+  if (!desc) return EA_ERR_NULL;
+  if (desc->B < 1 || desc->H < 1 || desc->N < 0 || (desc->d != 64 && desc->d != 128))
+    return EA_ERR_SHAPE;
+  if (desc->N > (1 << 24)) return EA_ERR_SHAPE;
+  if ((desc->in_dtype != EA_F32 && desc->in_dtype != EA_BF16) ||
+      (desc->out_dtype != EA_F32 && desc->out_dtype != EA_BF16))
+    return EA_ERR_DTYPE;
+  if (desc->tau_mode < EA_TAU_HIST_HALLEY || desc->tau_mode > EA_TAU_BISECT) return EA_ERR_UNSUPPORTED;
+  if (desc->max_iters < 0 || desc->max_iters > 250) return EA_ERR_UNSUPPORTED;
+  if (!(desc->tol >= 0.0f) || !(desc->tol < 1.0f)) return EA_ERR_UNSUPPORTED;
+  if (desc->flags & ~EA_FLAG_FORCE_DENSE) return EA_ERR_UNSUPPORTED;
+  if (s) {
+    s->B = desc->B;
+    s->H = desc->H;
+    s->N = desc->N;
+    s->d = desc->d;
+    s->esz = desc->in_dtype == EA_BF16 ? 2 : 4;
+    s->n_kt = (desc->N + kBK - 1) / kBK;
+    s->n_q32 = (desc->N + kBQ - 1) / kBQ;
+    s->n_qt128 = (desc->N + kBQW - 1) / kBQW;
+    s->n_kt128 = (desc->N + 127) / 128;
+    s->Np = s->n_kt * kBK;
+    s->BH = (long long)desc->B * desc->H;
+  }
+  return EA_OK;
+}
+
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_alpha(float alpha) {
+  if (!(alpha > 1.0f) || !(alpha <= 2.0f)) return EA_ERR_ALPHA;
+  return EA_OK;
+}
+
+size_t transposed_bytes(const Shape& s) { return align_up((size_t)s.BH * s.d * s.Np * s.esz, 256); }
+
+size_t workspace_bytes(const Shape& s) {
+  // forward: V^T;  backward: K^T, Q^T, dO^T and delta
+  const size_t t = transposed_bytes(s);
+  const size_t bwd = 3 * t + align_up((size_t)s.BH * s.N * sizeof(float), 256);
+  return bwd > t ? bwd : t;
+}
+
+int alpha_kind(float alpha) {
+  if (alpha == 1.5f) return AK15;
+  if (alpha == 2.0f) return AK20;
+  if (alpha == 1.25f) return AK125;
+  return AKGEN;
+}
+
+Params make_params(const ea_desc* desc, const Shape& s, float alpha, int causal) {
+  Params P;
+  P.N = s.N;
+  P.n_kt = s.n_kt;
+  P.n_q32 = s.n_q32;
+  P.causal = causal ? 1 : 0;
+  P.Np = s.Np;
+  P.alpha = alpha;
+  P.beta = (float)(1.0 / ((double)alpha - 1.0));
+  P.scale = (float)(((double)alpha - 1.0) / sqrt((double)s.d));
+  P.inv_sqrt_d = (float)(1.0 / sqrt((double)s.d));
+  P.mode = desc->tau_mode;
+  P.max_iters = desc->max_iters > 0 ? desc->max_iters : (desc->tau_mode == EA_TAU_BISECT ? 40 : 12);
+  P.flags = desc->flags;
+  P.tol = desc->tol > 0.0f ? desc->tol : 1e-6f;
+  P.out_bf16 = desc->out_dtype == EA_BF16 ? 1 : 0;
+  P.kt_cap = 0;
+  return P;
+}
+
+constexpr size_t kLdsBudget = 160 * 1024;
+
+// Records the caller's timing events around one stage (no-op without events).
+struct StageTimer {
+  void* const* ev;
+  hipStream_t st;
+  void begin(int s) const {
+    if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * s]), st);
+  }
+  void end(int s) const {
+    if (ev) (void)hipEventRecord(static_cast<hipEvent_t>(ev[2 * s + 1]), st);
+  }
+};
+
+template <typename F>
+int set_lds(F* fn, size_t bytes) {
+  if (bytes > 64 * 1024) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)bytes) != hipSuccess)
+      return EA_ERR_LAUNCH;
+  }
+  return EA_OK;
+}
+
+template <typename E, int D, int AK>
+int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const void* v, void* out,
+               float* tau, uint8_t* mask, float* aux, uint8_t* iters, void* ws, hipStream_t st,
+               StageTimer tm) {
+  const E* Q = static_cast<const E*>(q);
+  const E* K = static_cast<const E*>(k);
+  const E* V = static_cast<const E*>(v);
+  E* Vt = static_cast<E*>(ws);
+  if (s.N == 0) return EA_OK;
+  dim3 tg(s.Np / 64, D / 64, (unsigned)s.BH);
+  tm.begin(EA_STAGE_FWD_PREP);
+  hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, V, Vt, s.N, D, s.Np);
+  tm.end(EA_STAGE_FWD_PREP);
+
+  constexpr int BINS = (sizeof(E) == 4 && D == 128) ? 8 : 16;
+  constexpr int KS = D * (int)sizeof(E) + 16;
+  const size_t fixed = (size_t)kBK * KS + (size_t)kBQW * BINS * 16 + 64;
+  // per key tile: 4 f32 maxima + 4 candidate bytes + one list entry
+  size_t cap = (kLdsBudget - fixed) / (kWaves * 4 + kWaves + 2);
+  if (cap > 4096) cap = 4096;
+  P.kt_cap = (int)cap;
+  size_t tau_lds = fixed + cap * (kWaves * 4 + kWaves + 2) + 16;
+  if ((size_t)s.n_kt <= cap) {
+    // shrink to what this problem needs
+    P.kt_cap = s.n_kt + (s.n_kt & 1);
+    tau_lds = fixed + (size_t)P.kt_cap * (kWaves * 4 + kWaves + 2) + 16;
+  } else {
+    P.kt_cap = 0;
+    tau_lds = fixed + 16;
+  }
+  auto ktau = k_tau<E, D, AK, BINS>;
+  if (set_lds(ktau, tau_lds) != EA_OK) return EA_ERR_LAUNCH;
+  dim3 g(s.n_qt128, (unsigned)s.BH);
+  tm.begin(EA_STAGE_TAU);
+  hipLaunchKernelGGL(ktau, g, dim3(kThreads), tau_lds, st, Q, K, P, tau, mask, iters);
+  tm.end(EA_STAGE_TAU);
+
+  constexpr int VS = kBK * (int)sizeof(E) + 16;
+  const size_t pv_lds = (size_t)kBK * KS + (size_t)D * VS + kWaves * kMaskChunk;
+  auto kpv = k_pv<E, D, AK>;
+  if (set_lds(kpv, pv_lds) != EA_OK) return EA_ERR_LAUNCH;
+  tm.begin(EA_STAGE_PV);
+  hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, Vt, tau, mask, P, out, aux);
+  tm.end(EA_STAGE_PV);
+  return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+}
+
+template <typename E, int D, int AK>
+int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const void* v,
+               const void* dout, const float* tau, const uint8_t* mask, const float* aux, void* dq,
+               void* dk, void* dv, void* ws, hipStream_t st, StageTimer tm) {
+  const E* Q = static_cast<const E*>(q);
+  const E* K = static_cast<const E*>(k);
+  const E* V = static_cast<const E*>(v);
+  const E* dO = static_cast<const E*>(dout);
+  if (s.N == 0) return EA_OK;
+  char* w = static_cast<char*>(ws);
+  const size_t tb = transposed_bytes(s);
+  E* Kt = reinterpret_cast<E*>(w);
+  E* Qt = reinterpret_cast<E*>(w + tb);
+  E* dOt = reinterpret_cast<E*>(w + 2 * tb);
+  float* delta = reinterpret_cast<float*>(w + 3 * tb);
+  dim3 tg(s.Np / 64, D / 64, (unsigned)s.BH);
+  tm.begin(EA_STAGE_BWD_PREP);
+  hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, K, Kt, s.N, D, s.Np);
+  hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, Q, Qt, s.N, D, s.Np);
+  hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, dO, dOt, s.N, D, s.Np);
+  const long long rows = s.BH * s.N;
+  hipLaunchKernelGGL((k_delta<E, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, dO, aux,
+                     delta, rows);
+  tm.end(EA_STAGE_BWD_PREP);
+
+  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr int VS = kBK * (int)sizeof(E) + 16;
+  constexpr int TS = kBQ * (int)sizeof(E) + 16;
+  const size_t dq_lds = (size_t)2 * kBK * KS + (size_t)D * VS + kWaves * kMaskChunk;
+  auto kdq = k_bwd_dq<E, D, AK>;
+  if (set_lds(kdq, dq_lds) != EA_OK) return EA_ERR_LAUNCH;
+  tm.begin(EA_STAGE_DQ);
+  hipLaunchKernelGGL(kdq, dim3(s.n_qt128, (unsigned)s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO,
+                     Kt, tau, delta, mask, P, dq);
+  tm.end(EA_STAGE_DQ);
+
+  const size_t kv_lds = (size_t)2 * kBQ * KS + (size_t)2 * D * TS + 2 * kBQ * 4 + 2 * kMaskChunk + 16;
+  auto kkv = k_bwd_dkdv<E, D, AK>;
+  if (set_lds(kkv, kv_lds) != EA_OK) return EA_ERR_LAUNCH;
+  tm.begin(EA_STAGE_DKDV);
+  hipLaunchKernelGGL(kkv, dim3(s.n_kt128, (unsigned)s.BH), dim3(kThreads), kv_lds, st, Q, K, V, dO,
+                     Qt, dOt, tau, delta, mask, P, dk, dv);
+  tm.end(EA_STAGE_DKDV);
+  return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+}
+
+#define EA_DISPATCH(FN, ...)                                                          \
+  do {                                                                                \
+    const int ak = alpha_kind(alpha);                                                 \
+    if (desc->in_dtype == EA_BF16) {                                                  \
+      if (s.d == 64) {                                                                \
+        switch (ak) {                                                                 \
+          case AK15: return FN<__bf16, 64, AK15>(__VA_ARGS__);                        \
+          case AK20: return FN<__bf16, 64, AK20>(__VA_ARGS__);                        \
+          case AK125: return FN<__bf16, 64, AK125>(__VA_ARGS__);                      \
+          default: return FN<__bf16, 64, AKGEN>(__VA_ARGS__);                         \
+        }                                                                             \
+      } else {                                                                        \
+        switch (ak) {                                                                 \
+          case AK15: return FN<__bf16, 128, AK15>(__VA_ARGS__);                       \
+          case AK20: return FN<__bf16, 128, AK20>(__VA_ARGS__);                       \
+          case AK125: return FN<__bf16, 128, AK125>(__VA_ARGS__);                     \
+          default: return FN<__bf16, 128, AKGEN>(__VA_ARGS__);                        \
+        }                                                                             \
+      }                                                                               \
+    } else {                                                                          \
+      if (s.d == 64) {                                                                \
+        switch (ak) {                                                                 \
+          case AK15: return FN<float, 64, AK15>(__VA_ARGS__);                         \
+          case AK20: return FN<float, 64, AK20>(__VA_ARGS__);                         \
+          case AK125: return FN<float, 64, AK125>(__VA_ARGS__);                       \
+          default: return FN<float, 64, AKGEN>(__VA_ARGS__);                          \
+        }                                                                             \
+      } else {                                                                        \
+        switch (ak) {                                                                 \
+          case AK15: return FN<float, 128, AK15>(__VA_ARGS__);                        \
+          case AK20: return FN<float, 128, AK20>(__VA_ARGS__);                        \
+          case AK125: return FN<float, 128, AK125>(__VA_ARGS__);                      \
+          default: return FN<float, 128, AKGEN>(__VA_ARGS__);                         \
+        }                                                                             \
+      }                                                                               \
+    }                                                                                 \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t entmax_attn_workspace_bytes(const ea_desc* desc) {
+  Shape s;
+  if (check_desc(desc, &s) != EA_OK) return 0;
+  return workspace_bytes(s);
+}
+
+size_t entmax_attn_aux_bytes(const ea_desc* desc) {
+  Shape s;
+  if (check_desc(desc, &s) != EA_OK) return 0;
+  return (size_t)s.BH * s.N * s.d * sizeof(float);
+}
+
+int entmax_attn_mask_dims(const ea_desc* desc, int* n_qt, int* n_kt, int* bm, int* bn) {
+  Shape s;
+  int st = check_desc(desc, &s);
+  if (st != EA_OK) return st;
+  if (n_qt) *n_qt = s.n_q32;
+  if (n_kt) *n_kt = s.n_kt;
+  if (bm) *bm = kBQ;
+  if (bn) *bn = kBK;
+  return EA_OK;
+}
+
+int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, int causal, void* out,
+                    float* tau, uint8_t* block_mask, void* aux, uint8_t* tau_iters,
+                    const ea_desc* desc, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int st = check_desc(desc, &s);
+  if (st != EA_OK) return st;
+  if ((st = check_alpha(alpha)) != EA_OK) return st;
+  if (causal != 0 && causal != 1) return EA_ERR_UNSUPPORTED;
+  if (s.N > 0) {
+    if (!q || !k || !v || !out || !tau || !block_mask || !ws) return EA_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(tau) ||
+        misaligned(aux) || misaligned(ws))
+      return EA_ERR_ALIGN;
+    if (ws_bytes < workspace_bytes(s)) return EA_ERR_WORKSPACE;
+  }
+  Params P = make_params(desc, s, alpha, causal);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  EA_DISPATCH(launch_fwd, s, P, q, k, v, out, tau, block_mask, static_cast<float*>(aux), tau_iters, ws,
+              hs, StageTimer{desc->events, hs});
+}
+
+int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, int causal,
+                    const void* dout, const float* tau, const uint8_t* block_mask, const void* aux,
+                    void* dq, void* dk, void* dv, const ea_desc* desc, void* ws, size_t ws_bytes,
+                    void* stream) {
+  Shape s;
+  int st = check_desc(desc, &s);
+  if (st != EA_OK) return st;
+  if ((st = check_alpha(alpha)) != EA_OK) return st;
+  if (causal != 0 && causal != 1) return EA_ERR_UNSUPPORTED;
+  if (s.N > 0) {
+    if (!q || !k || !v || !dout || !tau || !block_mask || !aux || !dq || !dk || !dv || !ws)
+      return EA_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dout) || misaligned(tau) ||
+        misaligned(aux) || misaligned(dq) || misaligned(dk) || misaligned(dv) || misaligned(ws))
+      return EA_ERR_ALIGN;
+    if (ws_bytes < workspace_bytes(s)) return EA_ERR_WORKSPACE;
+  }
+  Params P = make_params(desc, s, alpha, causal);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  EA_DISPATCH(launch_bwd, s, P, q, k, v, dout, tau, block_mask, static_cast<const float*>(aux), dq, dk,
+              dv, ws, hs, StageTimer{desc->events, hs});
+}
+
+const char* entmax_attn_strerror(int status) {
+  switch (status) {
+    case EA_OK: return "success";
+    case EA_ERR_NULL: return "a required pointer is NULL";
+    case EA_ERR_SHAPE: return "invalid shape (B, H >= 1, N >= 0, d in {64, 128})";
+    case EA_ERR_DTYPE: return "invalid element type";
+    case EA_ERR_ALPHA: return "alpha must satisfy 1 < alpha <= 2";
+    case EA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case EA_ERR_WORKSPACE: return "workspace too small";
+    case EA_ERR_LAUNCH: return "kernel launch failed";
+    case EA_ERR_UNSUPPORTED: return "unsupported option (tau_mode, max_iters, tol, flags or causal)";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+/*
+ * entmax_attn.h -- C ABI of the fused alpha-entmax attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every batch b, head h and query row i:
+ *   s_ij  = q_i . k_j / sqrt(d)                       (j visible: all j, or j <= i when causal)
+ *   x_ij  = (alpha - 1) s_ij
+ *   tau_i : the unique root of  sum_j [x_ij - tau_i]_+^(1/(alpha-1)) = 1
+ *   p_ij  = [x_ij - tau_i]_+^(1/(alpha-1))
+ *   o_i   = sum_j p_ij v_j
+ * alpha = 2 is sparsemax, alpha -> 1 tends to softmax ("AdaSplash: Adaptive
+ * Sparse Flash Attention", ICML 2025 talk summary, section "Background").
+ * tau is found per row by Halley steps guarded by a bisection bracket (same
+ * page, "Accelerated Alpha-Entmax Transformation"), optionally started from a
+ * coarse per-row score histogram kept on chip ("AdaSplash-2: The Transformer
+ * Revolution We Didn't See Coming", section "Sparse Attention Makes Waves").
+ * S and P are never written to memory: Q tiles stay on chip and K/V tiles are
+ * streamed ("AdaSplash ...", section "AdaSplash: Fused GPU Kernel for
+ * Attention"), and key tiles whose probabilities are all zero are skipped in
+ * the output pass and in the backward (same page, "Exploiting Sparsity").
+ *
+ * Backward: with t = [x - tau]_+ and u = t^(1/(alpha-1) - 1) (= p^(2-alpha))
+ * on the support, dS = u * (dP - delta_i), delta_i = sum_j u_ij dP_ij / sum_j u_ij,
+ * dP = dO V^T, dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are dense, row-major [B, H, N, d] (d fastest), device memory,
+ *    16-byte aligned.  tau is float32 [B, H, N] in the x-domain above.
+ *  - in_dtype (q, k, v, dout) and out_dtype (out, dq, dk, dv) are EA_F32 or
+ *    EA_BF16.  d must be 64 or 128.  N >= 0 is arbitrary (ragged tails are
+ *    masked); B, H >= 1.  1 < alpha <= 2.
+ *  - The caller owns every buffer, including the workspace.  The library
+ *    allocates no device memory, keeps no mutable global state, and enqueues
+ *    all work asynchronously on `stream` (a hipStream_t; NULL = default
+ *    stream).  Calls on distinct buffers may run concurrently.
+ *  - Errors: every argument check happens before any work is enqueued, so a
+ *    call that returns an error has written nothing.  A failed launch returns
+ *    EA_ERR_LAUNCH.  No C++ exception crosses this interface.
+ */
+#ifndef ENTMAX_ATTN_H
+#define ENTMAX_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (0 = success). */
+#define EA_OK               0
+#define EA_ERR_NULL        -1   /* a required pointer is NULL */
+#define EA_ERR_SHAPE       -2   /* B, H < 1, N < 0, or d not in {64, 128} */
+#define EA_ERR_DTYPE       -3   /* unknown in_dtype / out_dtype */
+#define EA_ERR_ALPHA       -4   /* alpha outside (1, 2] or not finite */
+#define EA_ERR_ALIGN       -5   /* a tensor pointer is not 16-byte aligned */
+#define EA_ERR_WORKSPACE   -6   /* ws_bytes smaller than entmax_attn_workspace_bytes() */
+#define EA_ERR_LAUNCH      -7   /* the HIP runtime rejected a kernel launch */
+#define EA_ERR_UNSUPPORTED -8   /* unknown tau_mode, negative max_iters, bad tol or flags */
+
+/* Element types. */
+#define EA_F32  0
+#define EA_BF16 1
+
+/* tau initialisation / refinement modes. */
+#define EA_TAU_HIST_HALLEY   0  /* histogram-initialised Halley-bisection (default) */
+#define EA_TAU_HALLEY_BISECT 1  /* Halley-bisection started at the bracket's lower end */
+#define EA_TAU_BISECT        2  /* plain bisection of the bracket */
+
+/* Flags. */
+#define EA_FLAG_FORCE_DENSE  1  /* mark every visible tile active: no tile skipping */
+
+/* Tile shape of block_mask: one byte per (32 queries) x (64 keys). */
+#define EA_MASK_BM 32
+#define EA_MASK_BN 64
+
+typedef struct {
+  int32_t B, H, N, d;   /* batch, heads, sequence length, head dim (64 or 128) */
+  int32_t in_dtype;     /* EA_F32 | EA_BF16: q, k, v, dout */
+  int32_t out_dtype;    /* EA_F32 | EA_BF16: out, dq, dk, dv */
+  int32_t tau_mode;     /* EA_TAU_* */
+  int32_t max_iters;    /* refinement sweeps per row; 0 = default (12, or 40 for BISECT) */
+  float   tol;          /* stop when |f(tau)| <= tol; 0 = default 1e-6 */
+  int32_t flags;        /* EA_FLAG_* */
+  /* Optional timing hook: NULL, or 2 * EA_NUM_STAGES caller-created hipEvent_t
+   * handles.  Stage s (EA_STAGE_*) is bracketed by events[2s] and
+   * events[2s+1], recorded on `stream`; stages a call does not run are not
+   * recorded.  The library never creates or destroys events. */
+  void* const* events;
+} ea_desc;
+
+/* Stages, for the timing hook. */
+#define EA_STAGE_FWD_PREP  0   /* forward: V^T copy */
+#define EA_STAGE_TAU       1   /* forward: row maxima, histogram, Halley sweeps, block mask */
+#define EA_STAGE_PV        2   /* forward: O = P V and W = U V / sum U over active tiles */
+#define EA_STAGE_BWD_PREP  3   /* backward: K^T, Q^T, dO^T copies and delta */
+#define EA_STAGE_DQ        4   /* backward: dQ over active tiles */
+#define EA_STAGE_DKDV      5   /* backward: dK, dV over active tiles */
+#define EA_NUM_STAGES      6
+
+/* Bytes of device workspace both entry points need for `desc`: transposed
+ * copies of V (forward) or of K, Q, dO (backward) plus one float per row.
+ * O(B*H*N*d); never O(N^2).  Returns 0 for an invalid desc. */
+size_t entmax_attn_workspace_bytes(const ea_desc* desc);
+
+/* Bytes of the forward -> backward carry `aux`: float32 [B, H, N, d] holding
+ * w_i = sum_j u_ij v_j / sum_j u_ij, so that delta_i = dO_i . w_i.
+ * Returns 0 for an invalid desc. */
+size_t entmax_attn_aux_bytes(const ea_desc* desc);
+
+/* Shape of block_mask: [B, H, n_qt, n_kt] bytes with n_qt = ceil(N/bm),
+ * n_kt = ceil(N/bn).  Any output pointer may be NULL.  Returns a status. */
+int entmax_attn_mask_dims(const ea_desc* desc, int* n_qt, int* n_kt, int* bm, int* bn);
+
+/* Forward pass.
+ *  q, k, v     [B,H,N,d] in_dtype                     (read)
+ *  out         [B,H,N,d] out_dtype                    (written)
+ *  tau         float32 [B,H,N]                        (written)
+ *  block_mask  uint8 [B,H,n_qt,n_kt] (mask_dims)      (written): 1 where the
+ *              tile holds a visible entry with x > tau, 0 otherwise (a tile
+ *              marked 1 may still be all-zero only within float32 rounding).
+ *  aux         float32 [B,H,N,d] or NULL              (written if non-NULL; required by the backward)
+ *  tau_iters   uint8 [B,H,N] or NULL                  (written if non-NULL):
+ *              refinement sweeps that evaluated f(tau) for the row (the
+ *              row-max and histogram sweeps are not counted).
+ *  alpha       1 < alpha <= 2;  causal: 0 or 1.
+ *  ws          device workspace of ws_bytes >= entmax_attn_workspace_bytes(desc).
+ */
+int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, int causal,
+                    void* out, float* tau, uint8_t* block_mask, void* aux, uint8_t* tau_iters,
+                    const ea_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass.  tau, block_mask and aux must come from entmax_attn_fwd on the
+ * same q, k, v, alpha, causal and desc.
+ *  dout        [B,H,N,d] in_dtype                     (read)
+ *  dq, dk, dv  [B,H,N,d] out_dtype                    (written)
+ */
+int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, int causal,
+                    const void* dout, const float* tau, const uint8_t* block_mask, const void* aux,
+                    void* dq, void* dk, void* dv,
+                    const ea_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* entmax_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTMAX_ATTN_H */

@@ -1,0 +1,99 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+the header declares, plans workspace without N^2 terms, and rejects invalid
+arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import adaptive_sparse_flash_amd as A
+from adaptive_sparse_flash_amd import binding as Bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "entmax_attn.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(entmax_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = A.load_library()
+    names = header_functions()
+    assert set(names) == set(Bd.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define\s+(EA_\w+)\s+(-?\d+)", text))
+    assert int(consts["EA_F32"]) == Bd.EA_F32 and int(consts["EA_BF16"]) == Bd.EA_BF16
+    assert int(consts["EA_TAU_HIST_HALLEY"]) == Bd.EA_TAU_HIST_HALLEY
+    assert int(consts["EA_TAU_BISECT"]) == Bd.EA_TAU_BISECT
+    assert int(consts["EA_NUM_STAGES"]) == len(Bd.STAGES)
+    assert int(consts["EA_MASK_BM"]) == 32 and int(consts["EA_MASK_BN"]) == 64
+
+
+def test_desc_struct_layout():
+    # int32 x 9 + float + pointer, natural alignment
+    assert ctypes.sizeof(Bd.EaDesc) == 48
+
+
+def test_workspace_has_no_quadratic_term():
+    sizes = []
+    for n in (4096, 8192, 16384):
+        d = A.make_desc(1, 16, n, 128)
+        sizes.append(A.entmax_attn_workspace_bytes(d))
+    assert sizes[1] <= 2.01 * sizes[0] and sizes[2] <= 2.01 * sizes[1]
+    d = A.make_desc(2, 3, 1000, 64, out_dtype=1)
+    assert A.entmax_attn_aux_bytes(d) == 2 * 3 * 1000 * 64 * 4
+    assert A.entmax_attn_mask_dims(d) == (32, 16, 32, 64)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d", 96, -2), ("N", -1, -2), ("B", 0, -2), ("in_dtype", 7, -3), ("out_dtype", -1, -3),
+    ("tau_mode", 5, -8), ("max_iters", -1, -8), ("tol", -1.0, -8), ("flags", 8, -8)])
+def test_invalid_desc_rejected(field, value, status):
+    d = A.make_desc(1, 1, 128, 64)
+    setattr(d, field, value)
+    assert A.entmax_attn_workspace_bytes(d) == 0
+    lib = A.load_library()
+    st = lib.entmax_attn_fwd(None, None, None, 1.5, 0, None, None, None, None, None,
+                             ctypes.byref(d), None, 0, None)
+    assert st == status
+
+
+def _fwd(lib, d, alpha=1.5, causal=0, ptr=16, ws_bytes=1 << 30, null=None):
+    p = [ctypes.c_void_p(ptr)] * 8
+    if null is not None:
+        p[null] = None
+    return lib.entmax_attn_fwd(p[0], p[1], p[2], alpha, causal, p[3], p[4], p[5], None, None,
+                               ctypes.byref(d), p[6], ws_bytes, None)
+
+
+def test_argument_errors_before_launch():
+    lib = A.load_library()
+    d = A.make_desc(1, 2, 256, 64)
+    for alpha in (1.0, 0.5, 2.5, float("nan"), float("inf")):
+        assert _fwd(lib, d, alpha=alpha) == -4
+    assert _fwd(lib, d, causal=2) == -8
+    for i in range(7):
+        assert _fwd(lib, d, null=i) == -1
+    assert _fwd(lib, d, ptr=8) == -5
+    assert _fwd(lib, d, ws_bytes=16) == -6
+    st = lib.entmax_attn_bwd(None, None, None, 1.5, 0, None, None, None, None, None, None, None,
+                             ctypes.byref(d), None, 0, None)
+    assert st == -1
+    assert A.strerror(-6) == "workspace too small"
+    assert A.strerror(12345) == "unknown status"
+
+
+def test_empty_sequence_is_a_no_op():
+    lib = A.load_library()
+    d = A.make_desc(1, 1, 0, 64)
+    st = lib.entmax_attn_fwd(None, None, None, 1.5, 1, None, None, None, None, None,
+                             ctypes.byref(d), None, 0, None)
+    assert st == 0
