@@ -18,7 +18,7 @@ EA_OK = 0
 EA_F32, EA_BF16 = 0, 1
 EA_TAU_HIST_HALLEY, EA_TAU_HALLEY_BISECT, EA_TAU_BISECT = 0, 1, 2
 EA_FLAG_FORCE_DENSE = 1
-STAGES = ("fwd_prep", "tau", "pv", "bwd_prep", "dq", "dkdv")
+STAGES = ("fwd_prep", "rowmax", "tau", "pv", "bwd_prep", "dq", "dkdv")
 EA_NUM_STAGES = len(STAGES)
 TAU_MODES = {"hist": EA_TAU_HIST_HALLEY, "halley": EA_TAU_HALLEY_BISECT, "bisect": EA_TAU_BISECT}
 

@@ -48,7 +48,6 @@ constexpr int kWaves = 4;
 constexpr int kBQW = kBQ * kWaves;    // queries per workgroup (forward, dQ)
 constexpr int kBK = 64;               // keys per tile = mask column granularity
 constexpr int kThreads = kWave * kWaves;
-constexpr int kMaskChunk = 1024;      // key tiles of mask staged in LDS at once
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -60,11 +59,11 @@ enum AlphaKind { AK15 = 0, AK20 = 1, AK125 = 2, AKGEN = 3 };
 struct Params {
   int N, n_kt, n_q32, causal;
   int Np;                 // N rounded up to 64 (row length of transposed copies)
+  int BH;                 // batch * heads
   float alpha, beta, scale, inv_sqrt_d;
   int mode, max_iters, flags;
   float tol;
   int out_bf16;
-  int kt_cap;             // key tiles with LDS candidate state (0 = pruning off)
 };
 
 // ----------------------------------------------------------- fragments ---
@@ -278,181 +277,338 @@ __device__ __forceinline__ void load_qfrags(Frag<E> (&qf)[D / 16], const E* rowp
   }
 }
 
-__device__ __forceinline__ int qtile_of_block(const Params& P) {
-  // causal: heaviest query tiles first
-  return P.causal ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+// --------------------------------------------------- work distribution ---
+// Workgroups are dealt round robin to the 8 XCDs (block b runs on XCD b % 8).
+// When B*H is a multiple of 8 each XCD gets its own heads, so one XCD's L2
+// serves the K/V of few heads; inside an XCD (or globally otherwise) tiles of
+// different heads are interleaved by rank.  With heavy_first, rank 0 is the
+// tile with the most work (the last query tile when causal).
+__device__ __forceinline__ void map_tile(int n_tiles, int BH, bool heavy_first, int& bh, int& tile) {
+  const int b = blockIdx.x;
+  int rank;
+  if ((BH & 7) == 0) {
+    const int hx = BH >> 3, j = b >> 3;
+    bh = (b & 7) * hx + j % hx;
+    rank = j / hx;
+  } else {
+    bh = b % BH;
+    rank = b / BH;
+  }
+  tile = heavy_first ? n_tiles - 1 - rank : rank;
+}
+
+// ---------------------------------------------------- prefetch staging ---
+// A tile of ROWS rows x D elements staged global -> registers -> LDS, so the
+// global loads of the next tile overlap the MFMA work on the current one.
+template <typename E, int D, int ROWS, int NT = kThreads>
+struct RowStage {
+  static constexpr int CH = D * (int)sizeof(E) / 16;
+  static constexpr int PER = (ROWS * CH + NT - 1) / NT;
+  f32x4 r[PER];
+  __device__ __forceinline__ void load(const E* g, int row0, int N) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int rr = c / CH, cc = c - rr * CH;
+      const int gr = row0 + rr;
+      r[i] = f32x4{0, 0, 0, 0};
+      if (c < ROWS * CH && gr < N)
+        r[i] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(g + (size_t)gr * D) + cc * 16);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int lstride) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int rr = c / CH, cc = c - rr * CH;
+      if (c < ROWS * CH) *reinterpret_cast<f32x4*>(lds + rr * lstride + cc * 16) = r[i];
+    }
+  }
+};
+// Columns col0..col0+W of a transposed [D][Np] matrix (all in range).
+template <typename E, int D, int W, int NT = kThreads>
+struct ColStage {
+  static constexpr int CH = W * (int)sizeof(E) / 16;
+  static constexpr int PER = (D * CH + NT - 1) / NT;
+  f32x4 r[PER];
+  __device__ __forceinline__ void load(const E* gt, int Np, int col0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int rr = c / CH, cc = c - rr * CH;
+      r[i] = f32x4{0, 0, 0, 0};
+      if (c < D * CH)
+        r[i] = *reinterpret_cast<const f32x4*>(
+            reinterpret_cast<const char*>(gt + (size_t)rr * Np + col0) + cc * 16);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int lstride) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int rr = c / CH, cc = c - rr * CH;
+      if (c < D * CH) *reinterpret_cast<f32x4*>(lds + rr * lstride + cc * 16) = r[i];
+    }
+  }
+};
+
+// Compacts tiles base..base+len-1 whose wave bits (pred(w, t) for the four
+// waves) are not all zero into list[] / wbits[]; returns the count.  Every
+// thread of the workgroup must call it.  `flags` holds len bytes of scratch.
+template <typename Pred>
+__device__ __forceinline__ int build_list(int base, int len, Pred pred, short* list, uint8_t* wbits,
+                                          uint8_t* flags, int* counter) {
+  for (int i = threadIdx.x; i < len; i += kThreads) {
+    uint8_t b = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww)
+      if (pred(ww, base + i)) b |= (uint8_t)(1u << ww);
+    flags[i] = b;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int count = 0;
+    for (int b0 = 0; b0 < len; b0 += kWave) {
+      const int i = b0 + lane;
+      const uint8_t b = i < len ? flags[i] : 0;
+      const unsigned long long bal = __ballot(b != 0);
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (b) {
+        list[count + before] = (short)i;
+        wbits[count + before] = b;
+      }
+      count += __popcll(bal);
+    }
+    if (lane == 0) *counter = count;
+  }
+  __syncthreads();
+  return *counter;
+}
+
+// ---------------------------------------------------------- k_rowmax ---
+// The one full score sweep: per-row maxima of x = (alpha-1) q.k / sqrt(d)
+// and, per (32 queries) x (64 keys) tile, the maximum raw score (used to
+// prune key tiles that can never hold a nonzero probability).  Each wave
+// owns 64 queries (two B-operand blocks share every K fragment read from
+// LDS); the workgroup (256 queries) streams K tiles double-buffered.
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, const E* __restrict__ K,
+                                                     Params P, float* __restrict__ rowmax,
+                                                     float* __restrict__ tilemax) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int KS = D * (int)sizeof(E) + 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
+  const int N = P.N;
+  const int n_qt = (N + 255) / 256;
+  int bh, qtile;
+  map_tile(n_qt, P.BH, P.causal, bh, qtile);
+  const int q0 = qtile * 256;
+  const int wq0 = q0 + 64 * w;
+  const E* Qh = Q + (size_t)bh * N * D;
+  const E* Kh = K + (size_t)bh * N * D;
+
+  Frag<E> qf[2][D / 16];
+  int iq[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    iq[qb] = wq0 + 32 * qb + c32;
+    load_qfrags<E, D>(qf[qb], Qh + (size_t)iq[qb] * D, iq[qb] < N, h);
+  }
+  const int kt_end = P.causal ? (min(N - 1, q0 + 255) / kBK + 1) : P.n_kt;
+  const int kt_end_w = wq0 >= N ? 0 : (P.causal ? (min(N - 1, wq0 + 63) / kBK + 1) : P.n_kt);
+  const bool tail = wq0 + 64 > N;
+
+  float m[2] = {-INFINITY, -INFINITY};
+  RowStage<E, D, kBK> st;
+  if (kt_end > 0) {
+    st.load(Kh, 0, N);
+    st.store(smem, KS);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < kt_end; ++kt) {
+    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
+    if (kt < kt_end_w) {
+      const char* kl = smem + (kt & 1) * kBK * KS;
+      f32x16 acc[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          Frag<E> a;
+          ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
+          mma(acc[0][kb], a, qf[0][c]);
+          mma(acc[1][kb], a, qf[1][c]);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const bool need = tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0 + 32 * qb);
+        if (need) mask_T(acc[qb], kt * kBK, iq[qb], N, P.causal, h);
+        float tm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tm = fmaxf(tm, fmaxf(acc[qb][0][i], acc[qb][1][i]));
+        m[qb] = fmaxf(m[qb], tm);
+        const float wm = wave_max(tm);
+        const int r32 = (wq0 >> 5) + qb;
+        if (lane == 0 && r32 < P.n_q32) tilemax[((size_t)bh * P.n_q32 + r32) * P.n_kt + kt] = wm;
+      }
+    }
+    if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float mm = fmaxf(m[qb], __shfl_xor(m[qb], 32));
+    if (iq[qb] < N && h == 0) rowmax[(size_t)bh * N + iq[qb]] = mm * P.scale;
+  }
 }
 
 // ------------------------------------------------------------- k_tau ---
-// Per workgroup (128 queries): row maxima, optional histogram, Halley /
-// bisection sweeps, tau and the block mask.  Dynamic LDS layout:
-//   K tile [64][D] | histogram [128][BINS][2] u64 | tile max [4][cap] f32 |
-//   candidate [4][cap] u8 | candidate list [cap] i16 | counters
+// Per workgroup (128 queries, 32 per wave): bracket from the row maxima,
+// candidate key tiles from the tile maxima, histogram initialisation,
+// Halley / bisection sweeps over candidate tiles, tau, iteration counts and
+// the block mask.  Dynamic LDS: K double buffer | histogram [128][BINS][2] u64 |
+// list i16[kChunk] | wave bits u8[kChunk] | flags u8[kChunk] | per-wave state.
+constexpr int kChunk = 1024;   // key tiles listed at once
+
 template <typename E, int D, int AK, int BINS>
 __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
-                                                  Params P, float* __restrict__ tau_out,
+                                                  const float* __restrict__ rowmax,
+                                                  const float* __restrict__ tilemax, Params P,
+                                                  float* __restrict__ tau_out,
                                                   uint8_t* __restrict__ mask_out,
                                                   uint8_t* __restrict__ iters_out) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KS = D * (int)sizeof(E) + 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
-  const int bh = blockIdx.y;
-  const int qtile = qtile_of_block(P);
   const int N = P.N;
+  int bh, qtile;
+  map_tile((N + kBQW - 1) / kBQW, P.BH, P.causal, bh, qtile);
   const int q0 = qtile * kBQW;
   const int wq0 = q0 + kBQ * w;
   const int iq = wq0 + c32;
   const bool valid = iq < N;
   const bool wave_rows = wq0 < N;
+  const int r32 = qtile * kWaves + w;
   const E* Qh = Q + (size_t)bh * N * D;
   const E* Kh = K + (size_t)bh * N * D;
-  const int cap = P.kt_cap;
   const bool dense = (P.flags & EA_FLAG_FORCE_DENSE) != 0;
-  const bool prune = cap > 0 && P.n_kt <= cap && !dense;
 
-  char* ktile = smem;
-  unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem + kBK * KS);
-  float* tmx = reinterpret_cast<float*>(hist + kBQW * BINS * 2);
-  uint8_t* cand = reinterpret_cast<uint8_t*>(tmx + kWaves * cap);
-  short* list = reinterpret_cast<short*>(cand + kWaves * cap);
-  int* counters = reinterpret_cast<int*>(list + cap + (cap & 1));
+  char* kbuf = smem;                                                  // 2 x [64][KS]
+  unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem + 2 * kBK * KS);
+  short* list = reinterpret_cast<short*>(hist + kBQW * BINS * 2);
+  uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
+  uint8_t* flags = wbits + kChunk;
+  float* lo_wave = reinterpret_cast<float*>(flags + kChunk);          // [4]
+  int* kt_end_wave = reinterpret_cast<int*>(lo_wave + kWaves);        // [4]
+  int* counter = kt_end_wave + kWaves;
 
   Frag<E> qf[D / 16];
   load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
-
   const int wq_last = min(N - 1, wq0 + kBQ - 1);
   const int kt_end_w = !wave_rows ? 0 : (P.causal ? wq_last / kBK + 1 : P.n_kt);
-  const int wg_last = min(N - 1, q0 + kBQW - 1);
-  const int kt_end = P.causal ? wg_last / kBK + 1 : P.n_kt;
+  const int kt_end = P.causal ? (min(N - 1, q0 + kBQW - 1) / kBK + 1) : P.n_kt;
   const bool wave_has_tail = wq0 + kBQ > N;
 
-  // ---- sweep 0: row maxima (and per-(wave, tile) maxima for pruning)
-  float m = -INFINITY;
-  for (int kt = 0; kt < kt_end; ++kt) {
-    __syncthreads();
-    stage_rows<E, D>(ktile, KS, Kh, kt * kBK, kBK, N);
-    __syncthreads();
-    if (kt < kt_end_w) {
-      f32x16 acc[2];
-      scores_T<E, D>(acc, ktile, KS, qf, lane);
-      const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
-      if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
-      float tm = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tm = fmaxf(tm, fmaxf(acc[0][i], acc[1][i]));
-      m = fmaxf(m, tm);
-      if (prune) {
-        float wm = wave_max(tm);
-        if (lane == 0) tmx[w * cap + kt] = wm;
-      }
-    } else if (prune && lane == 0 && w < kWaves) {
-      tmx[w * cap + kt] = -INFINITY;
-    }
-  }
-  m = fmaxf(m, __shfl_xor(m, 32));
-
   // ---- provable bracket [lo, hi]:  f(max x - 1) >= 0 >= f(max x - n^(1-alpha))
-  const float xmax = m * P.scale;
+  const float xmax = valid ? rowmax[(size_t)bh * N + iq] : 0.0f;
   float lo = 0.0f, hi = 0.0f, tau = 0.0f;
   if (valid) {
-    double dl = (double)xmax - 1.0;
+    const double dl = (double)xmax - 1.0;
     lo = (float)dl;
     if ((double)lo > dl) lo = nextafterf(lo, -INFINITY);
-    double n = P.causal ? (double)(iq + 1) : (double)N;
-    double dh = (double)xmax - pow(n, 1.0 - (double)P.alpha);
+    const double n = P.causal ? (double)(iq + 1) : (double)N;
+    const double dh = (double)xmax - pow(n, 1.0 - (double)P.alpha);
     hi = (float)dh;
     if ((double)hi < dh) hi = nextafterf(hi, INFINITY);
     if (hi < lo) hi = lo;
   }
   bool conv = !valid;
   int iters = 0;
-
-  // ---- candidate tiles: some score of the tile can exceed the wave's lowest lo
   const float lo_w = wave_min(valid ? lo : INFINITY);
-  if (prune) {
-    for (int kt = lane; kt < kt_end; kt += kWave) {
-      bool c = kt < kt_end_w && tmx[w * cap + kt] * P.scale >= lo_w;
-      cand[w * cap + kt] = c ? 1 : 0;
-    }
+  if (lane == 0) {
+    lo_wave[w] = lo_w;
+    kt_end_wave[w] = kt_end_w;
   }
   __syncthreads();
-  if (prune && w == 0) {
-    int count = 0;
-    for (int base = 0; base < kt_end; base += kWave) {
-      int kt = base + lane;
-      bool bit = false;
-      if (kt < kt_end)
-        bit = cand[kt] | cand[cap + kt] | cand[2 * cap + kt] | cand[3 * cap + kt];
-      unsigned long long bal = __ballot(bit);
-      int before = __popcll(bal & ((1ull << lane) - 1ull));
-      if (bit) list[count + before] = (short)kt;
-      count += __popcll(bal);
-    }
-    if (lane == 0) counters[0] = count;
-  }
-  __syncthreads();
-  const int n_visit = prune ? counters[0] : kt_end;
+  // A key tile can hold a nonzero probability for wave ww only if its largest
+  // score reaches the wave's lowest lower bracket end (tau >= lo always).
+  const float* tmx = tilemax + ((size_t)bh * P.n_q32 + (size_t)qtile * kWaves) * P.n_kt;
+  auto cand = [&](int ww, int kt) -> bool {
+    if (kt >= kt_end_wave[ww]) return false;
+    if (dense) return true;
+    return tmx[(size_t)ww * P.n_kt + kt] * P.scale >= lo_wave[ww];
+  };
 
   // ---- histogram initialisation (AdaSplash-2)
   if (P.mode == EA_TAU_HIST_HALLEY) {
     for (int e = threadIdx.x; e < kBQW * BINS * 2; e += kThreads) hist[e] = 0ull;
     constexpr int SHIFT = 24 - (BINS == 16 ? 4 : 3);
-    for (int idx = 0; idx < n_visit; ++idx) {
-      const int kt = prune ? list[idx] : idx;
+    unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * BINS * 2;
+    for (int base = 0; base < kt_end; base += kChunk) {
+      const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
+      RowStage<E, D, kBK> st;
+      if (n > 0) {
+        st.load(Kh, (base + list[0]) * kBK, N);
+        st.store(kbuf, KS);
+      }
       __syncthreads();
-      stage_rows<E, D>(ktile, KS, Kh, kt * kBK, kBK, N);
-      __syncthreads();
-      const bool wc = prune ? cand[w * cap + kt] != 0 : kt < kt_end_w;
-      if (wc) {
-        f32x16 acc[2];
-        scores_T<E, D>(acc, ktile, KS, qf, lane);
-        const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
-        if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
-        unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * BINS * 2;
+      for (int i = 0; i < n; ++i) {
+        const int kt = base + list[i];
+        if (i + 1 < n) st.load(Kh, (base + list[i + 1]) * kBK, N);
+        if ((wbits[i] >> w) & 1) {
+          f32x16 acc[2];
+          scores_T<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane);
+          const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
+          if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float y = fmaf(acc[kb][i], P.scale, -lo);
-            if (y > 0.0f) {
-              unsigned Y = (unsigned)(y * 16777216.0f);
-              int b = min((int)(Y >> SHIFT), BINS - 1);
-              atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
-              atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
+            for (int j = 0; j < 16; ++j) {
+              const float y = fmaf(acc[kb][j], P.scale, -lo);
+              if (y > 0.0f) {
+                const unsigned Y = (unsigned)(y * 16777216.0f);
+                const int b = min((int)(Y >> SHIFT), BINS - 1);
+                atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
+                atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
+              }
             }
-          }
+        }
+        if (i + 1 < n) st.store(kbuf + ((i + 1) & 1) * kBK * KS, KS);
+        __syncthreads();
       }
     }
-    __syncthreads();
     if (valid) {
-      const unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * BINS * 2;
       const double inv24 = 1.0 / 16777216.0, inv48 = inv24 * inv24;
       const double beta = (double)P.beta;
       const bool exact = (AK == AK15 || AK == AK20);
-      double C = 0, S1 = 0, S2 = 0;       // moments of bins above the current edge
+      double C = 0, S1 = 0, S2 = 0;       // moments of the bins above the edge under test
       double f_hi = -1.0;                  // f at the upper edge of the bin under test
       int bstar = 0;
       double f_lo = 0, cstar = 0, Cs = 0, S1s = 0, S2s = 0;
       for (int b = BINS - 1; b >= 0; --b) {
-        unsigned long long h1 = hr[2 * b], h2 = hr[2 * b + 1];
-        double cb = (double)(h1 >> 40);
-        double s1 = (double)(h1 & ((1ull << 40) - 1ull)) * inv24;
-        double s2 = (double)h2 * inv48;
-        double e = (double)b / BINS;
-        double Cn = C + cb, S1n = S1 + s1, S2n = S2 + s2;
+        const unsigned long long h1 = hr[2 * b], h2 = hr[2 * b + 1];
+        const double cb = (double)(h1 >> 40);
+        const double s1 = (double)(h1 & ((1ull << 40) - 1ull)) * inv24;
+        const double s2 = (double)h2 * inv48;
+        const double e = (double)b / BINS;
+        const double Cn = C + cb, S1n = S1 + s1, S2n = S2 + s2;
         double f;
         if (AK == AK15) {
-          f = S2n - 2.0 * e * S1n + e * e * Cn - 1.0;
+          f = S2n - 2.0 * e * S1n + e * e * Cn - 1.0;      // exact at the edge
         } else if (AK == AK20) {
-          f = S1n - e * Cn - 1.0;
+          f = S1n - e * Cn - 1.0;                          // exact at the edge
         } else {
-          // general alpha: each bin's elements stand at their mean (estimate only)
+          // other alpha: each bin's elements stand at their mean (estimate only)
           f = -1.0;
           for (int bb = b; bb < BINS; ++bb) {
-            unsigned long long g1 = hr[2 * bb];
-            double cc = (double)(g1 >> 40);
+            const unsigned long long g1 = hr[2 * bb];
+            const double cc = (double)(g1 >> 40);
             if (cc > 0) {
-              double mean = (double)(g1 & ((1ull << 40) - 1ull)) * inv24 / cc;
+              const double mean = (double)(g1 & ((1ull << 40) - 1ull)) * inv24 / cc;
               f += cc * pow(fmax(mean - e, 0.0), beta);
             }
           }
@@ -474,8 +630,9 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
       const double eb = (double)bstar / BINS, eb1 = (double)(bstar + 1) / BINS;
       double t0 = -1.0;
       if (exact && cstar == 0.0 && Cs > 0.0) {
+        // the tau bin is empty: the support is exactly the bins above it
         if (AK == AK15) {
-          double disc = S1s * S1s - Cs * (S2s - 1.0);
+          const double disc = S1s * S1s - Cs * (S2s - 1.0);
           if (disc >= 0.0) t0 = (S1s - sqrt(disc)) / Cs;
         } else {
           t0 = (S1s - 1.0) / Cs;
@@ -483,14 +640,14 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         if (!(t0 >= eb && t0 <= eb1)) t0 = -1.0;
       }
       if (t0 < 0.0) {
-        double den = f_lo - f_hi;
+        const double den = f_lo - f_hi;
         t0 = den > 0.0 ? eb + (eb1 - eb) * (f_lo / den) : 0.5 * (eb + eb1);
       }
-      float t0x = (float)((double)lo + t0);
+      const float t0x = (float)((double)lo + t0);
       if (exact) {
         const float margin = fmaxf(1.0f, fabsf(xmax)) * 5e-7f + 1e-6f;
-        float nlo = (float)((double)lo + eb) - margin;
-        float nhi = (float)((double)lo + eb1) + margin;
+        const float nlo = (float)((double)lo + eb) - margin;
+        const float nhi = (float)((double)lo + eb1) + margin;
         if (nlo > lo) lo = nlo;
         if (nhi < hi) hi = nhi;
       }
@@ -502,8 +659,8 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     tau = 0.5f * (lo + hi);
   }
 
-  // ---- refinement sweeps (Halley-bisection or bisection)
-  uint8_t* mrow = mask_out + ((size_t)bh * P.n_q32 + (size_t)(qtile * kWaves + w)) * P.n_kt;
+  // ---- refinement sweeps (Halley-bisection or bisection) over candidate tiles
+  uint8_t* mrow = mask_out + ((size_t)bh * P.n_q32 + (size_t)r32) * P.n_kt;
   if (wave_rows) {
     for (int kt = lane; kt < P.n_kt; kt += kWave) mrow[kt] = (dense && kt < kt_end_w) ? 1 : 0;
   }
@@ -513,29 +670,37 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     const bool wave_busy = __ballot(!conv) != 0ull;
     if (!__syncthreads_or(wave_busy ? 1 : 0)) break;
     float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
-    for (int idx = 0; idx < n_visit; ++idx) {
-      const int kt = prune ? list[idx] : idx;
+    for (int base = 0; base < kt_end; base += kChunk) {
+      const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
+      RowStage<E, D, kBK> st;
+      if (n > 0) {
+        st.load(Kh, (base + list[0]) * kBK, N);
+        st.store(kbuf, KS);
+      }
       __syncthreads();
-      stage_rows<E, D>(ktile, KS, Kh, kt * kBK, kBK, N);
-      __syncthreads();
-      const bool wc = prune ? cand[w * cap + kt] != 0 : kt < kt_end_w;
-      if (wave_busy && wc) {
-        f32x16 acc[2];
-        scores_T<E, D>(acc, ktile, KS, qf, lane);
-        const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
-        if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
-        const float before = Ent<AK>::count(F0, F1, F2, cnt);
+      for (int i = 0; i < n; ++i) {
+        const int kt = base + list[i];
+        if (i + 1 < n) st.load(Kh, (base + list[i + 1]) * kBK, N);
+        if (wave_busy && ((wbits[i] >> w) & 1)) {
+          f32x16 acc[2];
+          scores_T<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane);
+          const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
+          if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
+          const float before = Ent<AK>::count(F0, F1, F2, cnt);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float t = clamp01(fmaf(acc[kb][i], P.scale, -tau));
-            Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
+            for (int j = 0; j < 16; ++j) {
+              const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
+              Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
+            }
+          if (!dense) {
+            const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
+            if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
           }
-        if (!dense) {
-          const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
-          if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
         }
+        if (i + 1 < n) st.store(kbuf + ((i + 1) & 1) * kBK * KS, KS);
+        __syncthreads();
       }
     }
     F0 += __shfl_xor(F0, 32);
@@ -599,20 +764,22 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
   constexpr int KS = D * (int)sizeof(E) + 16;
   constexpr int VS = kBK * (int)sizeof(E) + 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
-  const int bh = blockIdx.y;
-  const int qtile = qtile_of_block(P);
   const int N = P.N;
+  int bh, qtile;
+  map_tile((N + kBQW - 1) / kBQW, P.BH, P.causal, bh, qtile);
   const int wq0 = qtile * kBQW + kBQ * w;
   const int iq = wq0 + c32;
   const bool valid = iq < N;
-  const bool wave_rows = wq0 < N;
   const E* Qh = Q + (size_t)bh * N * D;
   const E* Kh = K + (size_t)bh * N * D;
   const E* Vth = Vt + (size_t)bh * D * P.Np;
 
-  char* ktile = smem;
-  char* vtile = smem + kBK * KS;
-  uint8_t* mstage = reinterpret_cast<uint8_t*>(vtile + D * VS);   // [4][kMaskChunk]
+  char* kbuf = smem;                                 // 2 x [64][KS]
+  char* vbuf = kbuf + 2 * kBK * KS;                  // 2 x [D][VS]
+  short* list = reinterpret_cast<short*>(vbuf + 2 * D * VS);
+  uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
+  uint8_t* flags = wbits + kChunk;
+  int* counter = reinterpret_cast<int*>(flags + kChunk);
 
   Frag<E> qf[D / 16];
   load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
@@ -628,41 +795,44 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
   }
   float usum = 0.0f;
 
-  const int row0 = qtile * kWaves;
-  for (int base = 0; base < P.n_kt; base += kMaskChunk) {
-    const int nk = min(kMaskChunk, P.n_kt - base);
-    __syncthreads();
-    for (int e = threadIdx.x; e < kWaves * kMaskChunk; e += kThreads) {
-      int ww = e / kMaskChunk, kk = e - ww * kMaskChunk;
-      uint8_t b = 0;
-      if (kk < nk && row0 + ww < P.n_q32) b = mask[((size_t)bh * P.n_q32 + row0 + ww) * P.n_kt + base + kk];
-      mstage[e] = b;
+  const size_t mrow0 = (size_t)bh * P.n_q32 + (size_t)qtile * kWaves;
+  auto active = [&](int ww, int kt) -> bool {
+    return (qtile * kWaves + ww) < P.n_q32 && mask[(mrow0 + ww) * P.n_kt + kt] != 0;
+  };
+  for (int base = 0; base < P.n_kt; base += kChunk) {
+    const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
+    RowStage<E, D, kBK> sk;
+    ColStage<E, D, kBK> sv;
+    if (n > 0) {
+      sk.load(Kh, (base + list[0]) * kBK, N);
+      sv.load(Vth, P.Np, (base + list[0]) * kBK);
+      sk.store(kbuf, KS);
+      sv.store(vbuf, VS);
     }
     __syncthreads();
-    for (int kk = 0; kk < nk; ++kk) {
-      const bool any = (mstage[kk] | mstage[kMaskChunk + kk] | mstage[2 * kMaskChunk + kk] |
-                        mstage[3 * kMaskChunk + kk]) != 0;
-      if (!any) continue;
-      const int kt = base + kk;
-      __syncthreads();
-      stage_rows<E, D>(ktile, KS, Kh, kt * kBK, kBK, N);
-      stage_cols<E, D, kBK>(vtile, VS, Vth, P.Np, kt * kBK);
-      __syncthreads();
-      if (wave_rows && mstage[w * kMaskChunk + kk]) {
+    for (int i = 0; i < n; ++i) {
+      const int kt = base + list[i];
+      if (i + 1 < n) {
+        sk.load(Kh, (base + list[i + 1]) * kBK, N);
+        sv.load(Vth, P.Np, (base + list[i + 1]) * kBK);
+      }
+      if ((wbits[i] >> w) & 1) {
+        const char* kl = kbuf + (i & 1) * kBK * KS;
+        const char* vl = vbuf + (i & 1) * D * VS;
         f32x16 acc[2];
-        scores_T<E, D>(acc, ktile, KS, qf, lane);
+        scores_T<E, D>(acc, kl, KS, qf, lane);
         const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
         if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
         f32x16 uu[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float t = clamp01(fmaf(acc[kb][i], P.scale, -tau));
+          for (int j = 0; j < 16; ++j) {
+            const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
             float p, u;
             Ent<AK>::pu(t, P.beta, p, u);
-            acc[kb][i] = p;
-            uu[kb][i] = u;
+            acc[kb][j] = p;
+            uu[kb][j] = u;
             usum += u;
           }
 #pragma unroll
@@ -677,7 +847,7 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
             const int koff = 32 * kb + 16 * s + 4 * h;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-              const E* vrow = reinterpret_cast<const E*>(vtile + (32 * db + c32) * VS);
+              const E* vrow = reinterpret_cast<const E*>(vl + (32 * db + c32) * VS);
               Frag<E> vf;
               ld4x2(vf, vrow + koff, vrow + koff + 8);
               mma(oacc[db], vf, pf);
@@ -688,6 +858,11 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
             }
           }
       }
+      if (i + 1 < n) {
+        sk.store(kbuf + ((i + 1) & 1) * kBK * KS, KS);
+        sv.store(vbuf + ((i + 1) & 1) * D * VS, VS);
+      }
+      __syncthreads();
     }
   }
   usum += __shfl_xor(usum, 32);
@@ -699,16 +874,16 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * db + 8 * g + 4 * h;
       const size_t off = ((size_t)bh * N + iq) * D + d0;
-      f32x4 o = f32x4{oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+      const f32x4 o = f32x4{oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
       if (P.out_bf16) {
-        bf16x4 ob = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+        const bf16x4 ob = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
         *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + off) = ob;
       } else {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = o;
       }
-      if (aux) {
-        f32x4 a = f32x4{uacc[db][4 * g] * inv_u, uacc[db][4 * g + 1] * inv_u,
-                        uacc[db][4 * g + 2] * inv_u, uacc[db][4 * g + 3] * inv_u};
+      if (want_aux) {
+        const f32x4 a = f32x4{uacc[db][4 * g] * inv_u, uacc[db][4 * g + 1] * inv_u,
+                              uacc[db][4 * g + 2] * inv_u, uacc[db][4 * g + 3] * inv_u};
         *reinterpret_cast<f32x4*>(aux + off) = a;
       }
     }
@@ -753,7 +928,7 @@ __global__ __launch_bounds__(256) void k_delta(const E* __restrict__ dO, const f
 // ---------------------------------------------------------- k_bwd_dq ---
 // Per workgroup (128 queries): dQ = dS K / sqrt(d) over active key tiles,
 // dS^T = U (dP^T - delta) with dP^T = V dO^T, all in the S^T layout.
-template <typename E, int D, int AK>
+template <typename E, int D, int AK, int NB>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Kt, const float* __restrict__ tau_in,
@@ -763,19 +938,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
   constexpr int KS = D * (int)sizeof(E) + 16;
   constexpr int VS = kBK * (int)sizeof(E) + 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
-  const int bh = blockIdx.y;
-  const int qtile = qtile_of_block(P);
   const int N = P.N;
+  int bh, qtile;
+  map_tile((N + kBQW - 1) / kBQW, P.BH, P.causal, bh, qtile);
   const int wq0 = qtile * kBQW + kBQ * w;
   const int iq = wq0 + c32;
   const bool valid = iq < N;
-  const bool wave_rows = wq0 < N;
   const size_t hoff = (size_t)bh * N * D;
+  const E* Kth = Kt + (size_t)bh * D * P.Np;
 
-  char* ktile = smem;
-  char* vtile = smem + kBK * KS;
-  char* kttile = vtile + kBK * KS;
-  uint8_t* mstage = reinterpret_cast<uint8_t*>(kttile + D * VS);
+  // NB = 2: double-buffered tiles; NB = 1 when two copies exceed the LDS
+  char* kbuf = smem;                                 // NB x [64][KS]
+  char* vbuf = kbuf + NB * kBK * KS;                 // NB x [64][KS]
+  char* tbuf = vbuf + NB * kBK * KS;                 // NB x [D][VS]
+  short* list = reinterpret_cast<short*>(tbuf + NB * D * VS);
+  uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
+  uint8_t* flags = wbits + kChunk;
+  int* counter = reinterpret_cast<int*>(flags + kChunk);
 
   Frag<E> qf[D / 16], of[D / 16];
   load_qfrags<E, D>(qf, Q + hoff + (size_t)iq * D, valid, h);
@@ -788,42 +967,49 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) gacc[db] = f32x16{};
 
-  const int row0 = qtile * kWaves;
-  for (int base = 0; base < P.n_kt; base += kMaskChunk) {
-    const int nk = min(kMaskChunk, P.n_kt - base);
-    __syncthreads();
-    for (int e = threadIdx.x; e < kWaves * kMaskChunk; e += kThreads) {
-      int ww = e / kMaskChunk, kk = e - ww * kMaskChunk;
-      uint8_t b = 0;
-      if (kk < nk && row0 + ww < P.n_q32) b = mask[((size_t)bh * P.n_q32 + row0 + ww) * P.n_kt + base + kk];
-      mstage[e] = b;
+  const size_t mrow0 = (size_t)bh * P.n_q32 + (size_t)qtile * kWaves;
+  auto active = [&](int ww, int kt) -> bool {
+    return (qtile * kWaves + ww) < P.n_q32 && mask[(mrow0 + ww) * P.n_kt + kt] != 0;
+  };
+  for (int base = 0; base < P.n_kt; base += kChunk) {
+    const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
+    RowStage<E, D, kBK> sk, sv;
+    ColStage<E, D, kBK> st;
+    if (n > 0) {
+      const int k0 = (base + list[0]) * kBK;
+      sk.load(K + hoff, k0, N);
+      sv.load(V + hoff, k0, N);
+      st.load(Kth, P.Np, k0);
+      sk.store(kbuf, KS);
+      sv.store(vbuf, KS);
+      st.store(tbuf, VS);
     }
     __syncthreads();
-    for (int kk = 0; kk < nk; ++kk) {
-      const bool any = (mstage[kk] | mstage[kMaskChunk + kk] | mstage[2 * kMaskChunk + kk] |
-                        mstage[3 * kMaskChunk + kk]) != 0;
-      if (!any) continue;
-      const int kt = base + kk;
-      __syncthreads();
-      stage_rows<E, D>(ktile, KS, K + hoff, kt * kBK, kBK, N);
-      stage_rows<E, D>(vtile, KS, V + hoff, kt * kBK, kBK, N);
-      stage_cols<E, D, kBK>(kttile, VS, Kt + (size_t)bh * D * P.Np, P.Np, kt * kBK);
-      __syncthreads();
-      if (wave_rows && mstage[w * kMaskChunk + kk]) {
+    for (int i = 0; i < n; ++i) {
+      const int kt = base + list[i];
+      if (i + 1 < n) {
+        const int k1 = (base + list[i + 1]) * kBK;
+        sk.load(K + hoff, k1, N);
+        sv.load(V + hoff, k1, N);
+        st.load(Kth, P.Np, k1);
+      }
+      if ((wbits[i] >> w) & 1) {
+        const int buf = NB == 2 ? (i & 1) : 0;
         f32x16 sacc[2], pacc[2];
-        scores_T<E, D>(sacc, ktile, KS, qf, lane);
-        scores_T<E, D>(pacc, vtile, KS, of, lane);
+        scores_T<E, D>(sacc, kbuf + buf * kBK * KS, KS, qf, lane);
+        scores_T<E, D>(pacc, vbuf + buf * kBK * KS, KS, of, lane);
         const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
         if (need) mask_T(sacc, kt * kBK, iq, N, P.causal, h);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float t = clamp01(fmaf(sacc[kb][i], P.scale, -tau));
+          for (int j = 0; j < 16; ++j) {
+            const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
             float p, u;
             Ent<AK>::pu(t, P.beta, p, u);
-            sacc[kb][i] = u * (pacc[kb][i] - dlt);
+            sacc[kb][j] = u * (pacc[kb][j] - dlt);
           }
+        const char* tl = tbuf + buf * D * VS;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -835,7 +1021,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
             const int koff = 32 * kb + 16 * s + 4 * h;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-              const E* krow = reinterpret_cast<const E*>(kttile + (32 * db + c32) * VS);
+              const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
               Frag<E> kf;
               ld4x2(kf, krow + koff, krow + koff + 8);
               mma(gacc[db], kf, sf);
@@ -843,6 +1029,14 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
             }
           }
       }
+      if (i + 1 < n) {
+        const int buf = NB == 2 ? ((i + 1) & 1) : 0;
+        if (NB == 1) __syncthreads();
+        sk.store(kbuf + buf * kBK * KS, KS);
+        sv.store(vbuf + buf * kBK * KS, KS);
+        st.store(tbuf + buf * D * VS, VS);
+      }
+      __syncthreads();
     }
   }
   if (!valid) return;
@@ -852,10 +1046,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
     for (int g = 0; g < 4; ++g) {
       const int d0 = 32 * db + 8 * g + 4 * h;
       const size_t off = hoff + (size_t)iq * D + d0;
-      f32x4 o = f32x4{gacc[db][4 * g], gacc[db][4 * g + 1], gacc[db][4 * g + 2], gacc[db][4 * g + 3]} *
-                P.inv_sqrt_d;
+      const f32x4 o =
+          f32x4{gacc[db][4 * g], gacc[db][4 * g + 1], gacc[db][4 * g + 2], gacc[db][4 * g + 3]} * P.inv_sqrt_d;
       if (P.out_bf16) {
-        bf16x4 ob = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+        const bf16x4 ob = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
         *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(dq) + off) = ob;
       } else {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(dq) + off) = o;
@@ -877,25 +1071,24 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KS = D * (int)sizeof(E) + 16;
   constexpr int TS = kBQ * (int)sizeof(E) + 16;
+  constexpr int STEP = 2 * kBQ * KS + 2 * D * TS + 2 * kBQ * 4;   // one pipeline buffer
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
-  const int bh = blockIdx.y;
-  const int ktile = blockIdx.x;
   const int N = P.N;
+  int bh, ktile;
+  map_tile((N + 127) / 128, P.BH, false, bh, ktile);
   const int kw0 = ktile * 128 + 32 * w;
   const int jk = kw0 + c32;
   const bool kvalid = jk < N;
   const bool wave_keys = kw0 < N;
-  const int kt64 = (ktile * 128) / kBK + (w >> 1);
   const size_t hoff = (size_t)bh * N * D;
+  const E* Qth = Qt + (size_t)bh * D * P.Np;
+  const E* dOth = dOt + (size_t)bh * D * P.Np;
 
-  char* qtl = smem;
-  char* otl = qtl + kBQ * KS;
-  char* qttl = otl + kBQ * KS;
-  char* ottl = qttl + D * TS;
-  float* taus = reinterpret_cast<float*>(ottl + D * TS);
-  float* dels = taus + kBQ;
-  short* list = reinterpret_cast<short*>(dels + kBQ);   // [kMaskChunk]
-  int* counters = reinterpret_cast<int*>(list + kMaskChunk);
+  // buffer b: Q rows | dO rows | Q^T cols | dO^T cols | tau[32] | delta[32]
+  short* list = reinterpret_cast<short*>(smem + 2 * STEP);
+  uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
+  uint8_t* flags = wbits + kChunk;
+  int* counter = reinterpret_cast<int*>(flags + kChunk);
 
   Frag<E> kf[D / 16], vf[D / 16];
   load_qfrags<E, D>(kf, K + hoff + (size_t)jk * D, kvalid, h);
@@ -909,94 +1102,116 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
   }
   const int ktA = (ktile * 128) / kBK, ktB = ktA + 1;
   const bool hasB = ktB < P.n_kt;
+  const size_t mbase = (size_t)bh * P.n_q32;
+  // waves 0, 1 cover key tile A (64 keys), waves 2, 3 key tile B
+  auto active = [&](int ww, int r) -> bool {
+    const int kt = ww < 2 ? ktA : ktB;
+    if (kt >= P.n_kt || (ktile * 128 + 32 * ww) >= N) return false;
+    return mask[(mbase + r) * P.n_kt + kt] != 0;
+  };
 
-  for (int rbase = 0; rbase < P.n_q32; rbase += kMaskChunk) {
-    const int nr = min(kMaskChunk, P.n_q32 - rbase);
-    __syncthreads();
-    if (w == 0) {
-      int count = 0;
-      for (int b0 = 0; b0 < nr; b0 += kWave) {
-        int r = rbase + b0 + lane;
-        bool bit = false;
-        if (b0 + lane < nr) {
-          const uint8_t* mr = mask + ((size_t)bh * P.n_q32 + r) * P.n_kt;
-          bit = mr[ktA] != 0 || (hasB && mr[ktB] != 0);
-        }
-        unsigned long long bal = __ballot(bit);
-        int before = __popcll(bal & ((1ull << lane) - 1ull));
-        if (bit) list[count + before] = (short)(b0 + lane);
-        count += __popcll(bal);
-      }
-      if (lane == 0) counters[0] = count;
+  struct Stage {
+    RowStage<E, D, kBQ> q, o;
+    ColStage<E, D, kBQ> qt, ot;
+    float ta, de;
+  } st;
+  auto load = [&](int r) {
+    const int qb0 = r * kBQ;
+    st.q.load(Q + hoff, qb0, N);
+    st.o.load(dO + hoff, qb0, N);
+    st.qt.load(Qth, P.Np, qb0);
+    st.ot.load(dOth, P.Np, qb0);
+    if (threadIdx.x < kBQ) {
+      const int qi = qb0 + threadIdx.x;
+      st.ta = qi < N ? tau_in[(size_t)bh * N + qi] : INFINITY;
+      st.de = qi < N ? delta_in[(size_t)bh * N + qi] : 0.0f;
+    }
+  };
+  auto store = [&](int b) {
+    char* p = smem + b * STEP;
+    st.q.store(p, KS);
+    st.o.store(p + kBQ * KS, KS);
+    st.qt.store(p + 2 * kBQ * KS, TS);
+    st.ot.store(p + 2 * kBQ * KS + D * TS, TS);
+    if (threadIdx.x < kBQ) {
+      float* f = reinterpret_cast<float*>(p + 2 * kBQ * KS + 2 * D * TS);
+      f[threadIdx.x] = st.ta;
+      f[kBQ + threadIdx.x] = st.de;
+    }
+  };
+
+  for (int base = 0; base < P.n_q32; base += kChunk) {
+    const int n = build_list(base, min(kChunk, P.n_q32 - base), active, list, wbits, flags, counter);
+    if (n > 0) {
+      load(base + list[0]);
+      store(0);
     }
     __syncthreads();
-    const int nact = counters[0];
-    for (int ia = 0; ia < nact; ++ia) {
-      const int r = rbase + list[ia];
+    for (int i = 0; i < n; ++i) {
+      const int r = base + list[i];
       const int qb0 = r * kBQ;
-      __syncthreads();
-      stage_rows<E, D>(qtl, KS, Q + hoff, qb0, kBQ, N);
-      stage_rows<E, D>(otl, KS, dO + hoff, qb0, kBQ, N);
-      stage_cols<E, D, kBQ>(qttl, TS, Qt + (size_t)bh * D * P.Np, P.Np, qb0);
-      stage_cols<E, D, kBQ>(ottl, TS, dOt + (size_t)bh * D * P.Np, P.Np, qb0);
-      if (threadIdx.x < kBQ) {
-        int qi = qb0 + threadIdx.x;
-        taus[threadIdx.x] = qi < N ? tau_in[(size_t)bh * N + qi] : INFINITY;
-        dels[threadIdx.x] = qi < N ? delta_in[(size_t)bh * N + qi] : 0.0f;
-      }
-      __syncthreads();
-      if (!wave_keys) continue;
-      if (mask[((size_t)bh * P.n_q32 + r) * P.n_kt + kt64] == 0) continue;
-      // S = Q K^T and dP = dO V^T: rows = the 32 queries, column = this lane's key
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      if (i + 1 < n) load(base + list[i + 1]);
+      if (wave_keys && ((wbits[i] >> w) & 1)) {
+        const char* p = smem + (i & 1) * STEP;
+        const char* qtl = p;
+        const char* otl = p + kBQ * KS;
+        const char* qttl = p + 2 * kBQ * KS;
+        const char* ottl = qttl + D * TS;
+        const float* taus = reinterpret_cast<const float*>(ottl + D * TS);
+        const float* dels = taus + kBQ;
+        // S = Q K^T and dP = dO V^T: rows = the 32 queries, column = this lane's key
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        Frag<E> a, b;
-        ld8(a, reinterpret_cast<const E*>(qtl + c32 * KS) + 16 * c + 8 * h);
-        mma(sacc, a, kf[c]);
-        ld8(b, reinterpret_cast<const E*>(otl + c32 * KS) + 16 * c + 8 * h);
-        mma(pacc, b, vf[c]);
-      }
+        for (int c = 0; c < D / 16; ++c) {
+          Frag<E> a, b;
+          ld8(a, reinterpret_cast<const E*>(qtl + c32 * KS) + 16 * c + 8 * h);
+          mma(sacc, a, kf[c]);
+          ld8(b, reinterpret_cast<const E*>(otl + c32 * KS) + 16 * c + 8 * h);
+          mma(pacc, b, vf[c]);
+        }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = acc_row(i, h);
-        const int qi = qb0 + qr;
-        float s = sacc[i];
-        if (!kvalid || qi >= N || (P.causal && jk > qi)) s = -INFINITY;
-        float t = clamp01(fmaf(s, P.scale, -taus[qr]));
-        float p, u;
-        Ent<AK>::pu(t, P.beta, p, u);
-        sacc[i] = p;
-        pacc[i] = u * (pacc[i] - dels[qr]);
-      }
+        for (int j = 0; j < 16; ++j) {
+          const int qr = acc_row(j, h);
+          const int qi = qb0 + qr;
+          float s = sacc[j];
+          if (!kvalid || qi >= N || (P.causal && jk > qi)) s = -INFINITY;
+          const float t = clamp01(fmaf(s, P.scale, -taus[qr]));
+          float pp, u;
+          Ent<AK>::pu(t, P.beta, pp, u);
+          sacc[j] = pp;
+          pacc[j] = u * (pacc[j] - dels[qr]);
+        }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        Frag<E> pf, sf;
-        from_acc(pf, sacc, 8 * s);
-        from_acc(sf, pacc, 8 * s);
-        const int qoff = 16 * s + 4 * h;
+        for (int s = 0; s < 2; ++s) {
+          Frag<E> pf, sf;
+          from_acc(pf, sacc, 8 * s);
+          from_acc(sf, pacc, 8 * s);
+          const int qoff = 16 * s + 4 * h;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const E* orow = reinterpret_cast<const E*>(ottl + (32 * db + c32) * TS);
-          const E* qrow = reinterpret_cast<const E*>(qttl + (32 * db + c32) * TS);
-          Frag<E> ob, qb;
-          ld4x2(ob, orow + qoff, orow + qoff + 8);
-          ld4x2(qb, qrow + qoff, qrow + qoff + 8);
-          mma(dva[db], pf, ob);
-          mma(dka[db], sf, qb);
+          for (int db = 0; db < D / 32; ++db) {
+            const E* orow = reinterpret_cast<const E*>(ottl + (32 * db + c32) * TS);
+            const E* qrow = reinterpret_cast<const E*>(qttl + (32 * db + c32) * TS);
+            Frag<E> ob, qb;
+            ld4x2(ob, orow + qoff, orow + qoff + 8);
+            ld4x2(qb, qrow + qoff, qrow + qoff + 8);
+            mma(dva[db], pf, ob);
+            mma(dka[db], sf, qb);
+          }
         }
       }
+      if (i + 1 < n) store((i + 1) & 1);
+      __syncthreads();
     }
   }
   if (!wave_keys) return;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = kw0 + acc_row(i, h);
-      if (j >= N) continue;
-      const size_t off = hoff + (size_t)j * D + 32 * db + c32;
-      const float vv = dva[db][i], kk = dka[db][i] * P.inv_sqrt_d;
+    for (int j = 0; j < 16; ++j) {
+      const int key = kw0 + acc_row(j, h);
+      if (key >= N) continue;
+      const size_t off = hoff + (size_t)key * D + 32 * db + c32;
+      const float vv = dva[db][j], kk = dka[db][j] * P.inv_sqrt_d;
       if (P.out_bf16) {
         reinterpret_cast<__bf16*>(dv)[off] = (__bf16)vv;
         reinterpret_cast<__bf16*>(dk)[off] = (__bf16)kk;
@@ -1010,17 +1225,19 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
 // =============================================================== host ===
 
 struct Shape {
-  int B, H, N, d, esz, n_kt, n_q32, n_qt128, n_kt128, Np;
-  long long BH;
+  int B, H, N, d, esz, n_kt, n_q32, n_qt128, n_qt256, n_kt128, Np;
+  int BH;
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kMaxN = 1 << 20;
 
 int check_desc(const ea_desc* desc, Shape* s) {
   if (!desc) return EA_ERR_NULL;
   if (desc->B < 1 || desc->H < 1 || desc->N < 0 || (desc->d != 64 && desc->d != 128))
     return EA_ERR_SHAPE;
-  if (desc->N > (1 << 24)) return EA_ERR_SHAPE;
+  if (desc->N > kMaxN || (long long)desc->B * desc->H > (1 << 20)) return EA_ERR_SHAPE;
   if ((desc->in_dtype != EA_F32 && desc->in_dtype != EA_BF16) ||
       (desc->out_dtype != EA_F32 && desc->out_dtype != EA_BF16))
     return EA_ERR_DTYPE;
@@ -1037,9 +1254,10 @@ int check_desc(const ea_desc* desc, Shape* s) {
     s->n_kt = (desc->N + kBK - 1) / kBK;
     s->n_q32 = (desc->N + kBQ - 1) / kBQ;
     s->n_qt128 = (desc->N + kBQW - 1) / kBQW;
+    s->n_qt256 = (desc->N + 255) / 256;
     s->n_kt128 = (desc->N + 127) / 128;
     s->Np = s->n_kt * kBK;
-    s->BH = (long long)desc->B * desc->H;
+    s->BH = desc->B * desc->H;
   }
   return EA_OK;
 }
@@ -1052,12 +1270,16 @@ int check_alpha(float alpha) {
 }
 
 size_t transposed_bytes(const Shape& s) { return align_up((size_t)s.BH * s.d * s.Np * s.esz, 256); }
+size_t row_bytes(const Shape& s) { return align_up((size_t)s.BH * s.N * sizeof(float), 256); }
+size_t tilemax_bytes(const Shape& s) {
+  return align_up((size_t)s.BH * s.n_q32 * s.n_kt * sizeof(float), 256);
+}
 
 size_t workspace_bytes(const Shape& s) {
-  // forward: V^T;  backward: K^T, Q^T, dO^T and delta
-  const size_t t = transposed_bytes(s);
-  const size_t bwd = 3 * t + align_up((size_t)s.BH * s.N * sizeof(float), 256);
-  return bwd > t ? bwd : t;
+  // forward: V^T | row maxima | tile maxima;  backward: K^T | Q^T | dO^T | delta
+  const size_t fwd = transposed_bytes(s) + row_bytes(s) + tilemax_bytes(s);
+  const size_t bwd = 3 * transposed_bytes(s) + row_bytes(s);
+  return bwd > fwd ? bwd : fwd;
 }
 
 int alpha_kind(float alpha) {
@@ -1074,6 +1296,7 @@ Params make_params(const ea_desc* desc, const Shape& s, float alpha, int causal)
   P.n_q32 = s.n_q32;
   P.causal = causal ? 1 : 0;
   P.Np = s.Np;
+  P.BH = s.BH;
   P.alpha = alpha;
   P.beta = (float)(1.0 / ((double)alpha - 1.0));
   P.scale = (float)(((double)alpha - 1.0) / sqrt((double)s.d));
@@ -1083,11 +1306,8 @@ Params make_params(const ea_desc* desc, const Shape& s, float alpha, int causal)
   P.flags = desc->flags;
   P.tol = desc->tol > 0.0f ? desc->tol : 1e-6f;
   P.out_bf16 = desc->out_dtype == EA_BF16 ? 1 : 0;
-  P.kt_cap = 0;
   return P;
 }
-
-constexpr size_t kLdsBudget = 160 * 1024;
 
 // Records the caller's timing events around one stage (no-op without events).
 struct StageTimer {
@@ -1103,6 +1323,7 @@ struct StageTimer {
 
 template <typename F>
 int set_lds(F* fn, size_t bytes) {
+  if (bytes > 160 * 1024) return EA_ERR_UNSUPPORTED;
   if (bytes > 64 * 1024) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)bytes) != hipSuccess)
@@ -1118,40 +1339,38 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   const E* Q = static_cast<const E*>(q);
   const E* K = static_cast<const E*>(k);
   const E* V = static_cast<const E*>(v);
-  E* Vt = static_cast<E*>(ws);
   if (s.N == 0) return EA_OK;
-  dim3 tg(s.Np / 64, D / 64, (unsigned)s.BH);
+  char* w = static_cast<char*>(ws);
+  E* Vt = reinterpret_cast<E*>(w);
+  float* rowmax = reinterpret_cast<float*>(w + transposed_bytes(s));
+  float* tilemax = reinterpret_cast<float*>(w + transposed_bytes(s) + row_bytes(s));
+  int rc;
+
   tm.begin(EA_STAGE_FWD_PREP);
-  hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, V, Vt, s.N, D, s.Np);
+  hipLaunchKernelGGL(k_transpose<E>, dim3(s.Np / 64, D / 64, s.BH), dim3(256), 0, st, V, Vt, s.N, D, s.Np);
   tm.end(EA_STAGE_FWD_PREP);
 
-  constexpr int BINS = (sizeof(E) == 4 && D == 128) ? 8 : 16;
   constexpr int KS = D * (int)sizeof(E) + 16;
-  const size_t fixed = (size_t)kBK * KS + (size_t)kBQW * BINS * 16 + 64;
-  // per key tile: 4 f32 maxima + 4 candidate bytes + one list entry
-  size_t cap = (kLdsBudget - fixed) / (kWaves * 4 + kWaves + 2);
-  if (cap > 4096) cap = 4096;
-  P.kt_cap = (int)cap;
-  size_t tau_lds = fixed + cap * (kWaves * 4 + kWaves + 2) + 16;
-  if ((size_t)s.n_kt <= cap) {
-    // shrink to what this problem needs
-    P.kt_cap = s.n_kt + (s.n_kt & 1);
-    tau_lds = fixed + (size_t)P.kt_cap * (kWaves * 4 + kWaves + 2) + 16;
-  } else {
-    P.kt_cap = 0;
-    tau_lds = fixed + 16;
-  }
+  const size_t rm_lds = (size_t)2 * kBK * KS;
+  auto krm = k_rowmax<E, D>;
+  if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
+  tm.begin(EA_STAGE_ROWMAX);
+  hipLaunchKernelGGL(krm, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, tilemax);
+  tm.end(EA_STAGE_ROWMAX);
+
+  constexpr int BINS = 16;
+  const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)kBQW * BINS * 16 + 4 * kChunk + 64;
   auto ktau = k_tau<E, D, AK, BINS>;
-  if (set_lds(ktau, tau_lds) != EA_OK) return EA_ERR_LAUNCH;
-  dim3 g(s.n_qt128, (unsigned)s.BH);
+  if ((rc = set_lds(ktau, tau_lds)) != EA_OK) return rc;
+  const dim3 g(s.n_qt128 * s.BH);
   tm.begin(EA_STAGE_TAU);
-  hipLaunchKernelGGL(ktau, g, dim3(kThreads), tau_lds, st, Q, K, P, tau, mask, iters);
+  hipLaunchKernelGGL(ktau, g, dim3(kThreads), tau_lds, st, Q, K, rowmax, tilemax, P, tau, mask, iters);
   tm.end(EA_STAGE_TAU);
 
   constexpr int VS = kBK * (int)sizeof(E) + 16;
-  const size_t pv_lds = (size_t)kBK * KS + (size_t)D * VS + kWaves * kMaskChunk;
+  const size_t pv_lds = (size_t)2 * kBK * KS + (size_t)2 * D * VS + 4 * kChunk + 16;
   auto kpv = k_pv<E, D, AK>;
-  if (set_lds(kpv, pv_lds) != EA_OK) return EA_ERR_LAUNCH;
+  if ((rc = set_lds(kpv, pv_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_PV);
   hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, Vt, tau, mask, P, out, aux);
   tm.end(EA_STAGE_PV);
@@ -1173,12 +1392,13 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
   E* Qt = reinterpret_cast<E*>(w + tb);
   E* dOt = reinterpret_cast<E*>(w + 2 * tb);
   float* delta = reinterpret_cast<float*>(w + 3 * tb);
-  dim3 tg(s.Np / 64, D / 64, (unsigned)s.BH);
+  int rc;
+  const dim3 tg(s.Np / 64, D / 64, s.BH);
   tm.begin(EA_STAGE_BWD_PREP);
   hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, K, Kt, s.N, D, s.Np);
   hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, Q, Qt, s.N, D, s.Np);
   hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, dO, dOt, s.N, D, s.Np);
-  const long long rows = s.BH * s.N;
+  const long long rows = (long long)s.BH * s.N;
   hipLaunchKernelGGL((k_delta<E, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, dO, aux,
                      delta, rows);
   tm.end(EA_STAGE_BWD_PREP);
@@ -1186,20 +1406,21 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
   constexpr int KS = D * (int)sizeof(E) + 16;
   constexpr int VS = kBK * (int)sizeof(E) + 16;
   constexpr int TS = kBQ * (int)sizeof(E) + 16;
-  const size_t dq_lds = (size_t)2 * kBK * KS + (size_t)D * VS + kWaves * kMaskChunk;
-  auto kdq = k_bwd_dq<E, D, AK>;
-  if (set_lds(kdq, dq_lds) != EA_OK) return EA_ERR_LAUNCH;
+  constexpr int NB = (4 * kBK * KS + 2 * D * VS + 4 * kChunk + 16) <= 160 * 1024 ? 2 : 1;
+  const size_t dq_lds = (size_t)NB * (2 * kBK * KS + D * VS) + 4 * kChunk + 16;
+  auto kdq = k_bwd_dq<E, D, AK, NB>;
+  if ((rc = set_lds(kdq, dq_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_DQ);
-  hipLaunchKernelGGL(kdq, dim3(s.n_qt128, (unsigned)s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO,
-                     Kt, tau, delta, mask, P, dq);
+  hipLaunchKernelGGL(kdq, dim3(s.n_qt128 * s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO, Kt, tau,
+                     delta, mask, P, dq);
   tm.end(EA_STAGE_DQ);
 
-  const size_t kv_lds = (size_t)2 * kBQ * KS + (size_t)2 * D * TS + 2 * kBQ * 4 + 2 * kMaskChunk + 16;
+  const size_t kv_lds = (size_t)2 * (2 * kBQ * KS + 2 * D * TS + 2 * kBQ * 4) + 4 * kChunk + 16;
   auto kkv = k_bwd_dkdv<E, D, AK>;
-  if (set_lds(kkv, kv_lds) != EA_OK) return EA_ERR_LAUNCH;
+  if ((rc = set_lds(kkv, kv_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_DKDV);
-  hipLaunchKernelGGL(kkv, dim3(s.n_kt128, (unsigned)s.BH), dim3(kThreads), kv_lds, st, Q, K, V, dO,
-                     Qt, dOt, tau, delta, mask, P, dk, dv);
+  hipLaunchKernelGGL(kkv, dim3(s.n_kt128 * s.BH), dim3(kThreads), kv_lds, st, Q, K, V, dO, Qt, dOt, tau,
+                     delta, mask, P, dk, dv);
   tm.end(EA_STAGE_DKDV);
   return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }

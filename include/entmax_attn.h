@@ -28,7 +28,7 @@
  *    16-byte aligned.  tau is float32 [B, H, N] in the x-domain above.
  *  - in_dtype (q, k, v, dout) and out_dtype (out, dq, dk, dv) are EA_F32 or
  *    EA_BF16.  d must be 64 or 128.  N >= 0 is arbitrary (ragged tails are
- *    masked); B, H >= 1.  1 < alpha <= 2.
+ *    masked, N <= 2^20); B, H >= 1.  1 < alpha <= 2.
  *  - The caller owns every buffer, including the workspace.  The library
  *    allocates no device memory, keeps no mutable global state, and enqueues
  *    all work asynchronously on `stream` (a hipStream_t; NULL = default
@@ -91,16 +91,18 @@ typedef struct {
 
 /* Stages, for the timing hook. */
 #define EA_STAGE_FWD_PREP  0   /* forward: V^T copy */
-#define EA_STAGE_TAU       1   /* forward: row maxima, histogram, Halley sweeps, block mask */
-#define EA_STAGE_PV        2   /* forward: O = P V and W = U V / sum U over active tiles */
-#define EA_STAGE_BWD_PREP  3   /* backward: K^T, Q^T, dO^T copies and delta */
-#define EA_STAGE_DQ        4   /* backward: dQ over active tiles */
-#define EA_STAGE_DKDV      5   /* backward: dK, dV over active tiles */
-#define EA_NUM_STAGES      6
+#define EA_STAGE_ROWMAX    1   /* forward: the full score sweep (row and tile maxima) */
+#define EA_STAGE_TAU       2   /* forward: histogram and Halley sweeps over candidate tiles, block mask */
+#define EA_STAGE_PV        3   /* forward: O = P V and W = U V / sum U over active tiles */
+#define EA_STAGE_BWD_PREP  4   /* backward: K^T, Q^T, dO^T copies and delta */
+#define EA_STAGE_DQ        5   /* backward: dQ over active tiles */
+#define EA_STAGE_DKDV      6   /* backward: dK, dV over active tiles */
+#define EA_NUM_STAGES      7
 
 /* Bytes of device workspace both entry points need for `desc`: transposed
- * copies of V (forward) or of K, Q, dO (backward) plus one float per row.
- * O(B*H*N*d); never O(N^2).  Returns 0 for an invalid desc. */
+ * copies of V (forward) or of K, Q, dO (backward), one float per row, and
+ * (forward) one float per block_mask tile.  O(B*H*N*d + B*H*n_qt*n_kt); no
+ * N^2-element buffer.  Returns 0 for an invalid desc. */
 size_t entmax_attn_workspace_bytes(const ea_desc* desc);
 
 /* Bytes of the forward -> backward carry `aux`: float32 [B, H, N, d] holding
