@@ -38,6 +38,8 @@
 #include <math.h>
 #include <float.h>
 
+#include <type_traits>
+
 #include "entmax_attn.h"
 
 namespace {
@@ -150,6 +152,23 @@ __device__ __forceinline__ float wave_min(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
   return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Maximum over the 64 lanes (wave-uniform result): DPP inside each 16-lane
+// row (xor 1, xor 2, half mirror, mirror), then the four row results.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // ------------------------------------------------------ entmax powers ---
@@ -417,7 +436,9 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   }
   const int kt_end = P.causal ? (min(N - 1, q0 + 255) / kBK + 1) : P.n_kt;
   const int kt_end_w = wq0 >= N ? 0 : (P.causal ? (min(N - 1, wq0 + 63) / kBK + 1) : P.n_kt);
-  const bool tail = wq0 + 64 > N;
+  // Tiles below kt_full are fully visible to every query of the workgroup and
+  // lie inside [0, N): they need no masking.  Only the diagonal / tail tiles do.
+  const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
 
   float m[2] = {-INFINITY, -INFINITY};
   RowStage<E, D, kBK> st;
@@ -426,36 +447,46 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
     st.store(smem, KS);
   }
   __syncthreads();
-  for (int kt = 0; kt < kt_end; ++kt) {
-    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
-    if (kt < kt_end_w) {
-      const char* kl = smem + (kt & 1) * kBK * KS;
-      f32x16 acc[2][2];
+
+  // one tile: scores for both query blocks, optional masking, maxima
+  auto tile = [&](int kt, auto masked) {
+    const char* kl = smem + (kt & 1) * kBK * KS;
+    f32x16 acc[2][2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
+    for (int qb = 0; qb < 2; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
+    for (int c = 0; c < D / 16; ++c) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          Frag<E> a;
-          ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
-          mma(acc[0][kb], a, qf[0][c]);
-          mma(acc[1][kb], a, qf[1][c]);
-        }
-      }
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const bool need = tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0 + 32 * qb);
-        if (need) mask_T(acc[qb], kt * kBK, iq[qb], N, P.causal, h);
-        float tm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tm = fmaxf(tm, fmaxf(acc[qb][0][i], acc[qb][1][i]));
-        m[qb] = fmaxf(m[qb], tm);
-        const float wm = wave_max(tm);
-        const int r32 = (wq0 >> 5) + qb;
-        if (lane == 0 && r32 < P.n_q32) tilemax[((size_t)bh * P.n_q32 + r32) * P.n_kt + kt] = wm;
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<E> a;
+        ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
+        mma(acc[0][kb], a, qf[0][c]);
+        mma(acc[1][kb], a, qf[1][c]);
       }
     }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if constexpr (decltype(masked)::value) mask_T(acc[qb], kt * kBK, iq[qb], N, P.causal, h);
+      float tm = fmaxf(acc[qb][0][0], acc[qb][1][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) tm = fmaxf(tm, fmaxf(acc[qb][0][i], acc[qb][1][i]));
+      m[qb] = fmaxf(m[qb], tm);
+      const float wm = wave_max_dpp(tm);
+      const int r32 = (wq0 >> 5) + qb;
+      if (lane == 0 && r32 < P.n_q32) tilemax[((size_t)bh * P.n_q32 + r32) * P.n_kt + kt] = wm;
+    }
+  };
+
+  int kt = 0;
+  for (; kt < kt_full; ++kt) {
+    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
+    tile(kt, std::false_type{});
+    if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
+    __syncthreads();
+  }
+  for (; kt < kt_end; ++kt) {
+    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
+    if (kt < kt_end_w) tile(kt, std::true_type{});
     if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
     __syncthreads();
   }

@@ -254,9 +254,9 @@ def tile_margins(q, k, alpha: float, causal: bool, tau, bm: int, bn: int):
         for qt in range(nqt):
             i0, i1 = qt * bm, min(n, qt * bm + bm)
             x = scores(qh[h, i0:i1], kh[h], alpha, causal, i0) - tauh[h, i0:i1, None]
-            for kt in range(nkt):
-                j0, j1 = kt * bn, min(n, kt * bn + bn)
-                m[h, qt, kt] = np.max(x[:, j0:j1])
+            colmax = np.max(x, axis=0)                       # per key, over the tile's rows
+            pad = np.full(nkt * bn - n, -np.inf)
+            m[h, qt] = np.max(np.concatenate([colmax, pad]).reshape(nkt, bn), axis=1)
     return m.reshape(lead + (nqt, nkt))
 
 
