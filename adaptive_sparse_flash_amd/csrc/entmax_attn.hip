@@ -99,6 +99,31 @@ __device__ __forceinline__ void ld4x2(Frag<float>& f, const float* p0, const flo
   f.a = *reinterpret_cast<const f32x4*>(p0);
   f.b = *reinterpret_cast<const f32x4*>(p1);
 }
+// LDS row stride (bytes) of a tile of D-element rows.  bf16 rows are padded by
+// 48 bytes: consecutive rows then start 48 bytes apart modulo the 256-byte bank
+// period, which keeps both access patterns used on these tiles conflict free
+// (16 lanes reading 16 rows with ds_read_b128, and 32 lanes reading 4 rows x
+// 64 bytes with ds_read_b64_tr_b16).  fp32 rows are padded by 16 bytes.
+template <typename E, int D>
+constexpr int row_stride() { return D * (int)sizeof(E) + (sizeof(E) == 2 ? 48 : 16); }
+
+// Operand fragment whose 8 contraction elements run down one column of a
+// row-major bf16 LDS tile: rows r0 + {0,1,2,3} and r0 + 8 + {0,1,2,3} (the
+// permuted key order of the score accumulators), column col0 + (lane & 31).
+// ds_read_b64_tr_b16 gives lane i of each 16-lane group element i % 4 of the
+// 8-byte chunks addressed by lanes 4j + i / 4 of that group (j = 0..3), so
+// lane r of a group addresses row r0 + r / 4, column col0 + 16 * half + 4 * (r % 4).
+__device__ __forceinline__ void ld_col8(Frag<__bf16>& f, const char* tile, int rs, int r0, int col0,
+                                        int lane) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int g = lane & 15;
+  const char* p = tile + (r0 + (g >> 2)) * rs + (col0 + 16 * ((lane >> 4) & 1) + 4 * (g & 3)) * 2;
+  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * rs));
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ float frag_get(const Frag<__bf16>& f, int j) { return (float)f.v[j]; }
+__device__ __forceinline__ float frag_get(const Frag<float>& f, int j) { return j < 4 ? f.a[j] : f.b[j - 4]; }
 // accumulator registers r[0..7] -> operand fragment
 __device__ __forceinline__ void from_acc(Frag<__bf16>& f, const f32x16& acc, int base) {
 #pragma unroll
@@ -416,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
                                                      Params P, float* __restrict__ rowmax,
                                                      float* __restrict__ tilemax) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr int KS = row_stride<E, D>();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
   const int n_qt = (N + 255) / 256;
@@ -513,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
                                                   uint8_t* __restrict__ mask_out,
                                                   uint8_t* __restrict__ iters_out) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr int KS = row_stride<E, D>();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
   int bh, qtile;
@@ -785,15 +810,19 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
 // Per workgroup (128 queries): O = P V and W = (U V) / sum(U) over the
 // active key tiles of the block mask.  U = t^(beta-1) is the entmax
 // Jacobian weight; W carries delta_i = dO_i . W_i to the backward.
+// bf16: V tiles are staged as rows and read down their columns with
+// transposed LDS reads; fp32: Vsrc is a V^T copy [BH][D][Np].
 template <typename E, int D, int AK>
 __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const E* __restrict__ K,
-                                                 const E* __restrict__ Vt,
+                                                 const E* __restrict__ Vsrc,
                                                  const float* __restrict__ tau_in,
                                                  const uint8_t* __restrict__ mask, Params P,
                                                  void* __restrict__ out, float* __restrict__ aux) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int KS = D * (int)sizeof(E) + 16;
-  constexpr int VS = kBK * (int)sizeof(E) + 16;
+  constexpr bool kTr = sizeof(E) == 2;
+  constexpr int KS = row_stride<E, D>();
+  constexpr int VS = kTr ? KS : kBK * (int)sizeof(E) + 16;
+  constexpr int VT = kTr ? kBK * KS : D * VS;      // bytes of one staged V tile
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
   int bh, qtile;
@@ -803,11 +832,11 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
   const bool valid = iq < N;
   const E* Qh = Q + (size_t)bh * N * D;
   const E* Kh = K + (size_t)bh * N * D;
-  const E* Vth = Vt + (size_t)bh * D * P.Np;
+  const E* Vh = kTr ? Vsrc + (size_t)bh * N * D : Vsrc + (size_t)bh * D * P.Np;
 
   char* kbuf = smem;                                 // 2 x [64][KS]
-  char* vbuf = kbuf + 2 * kBK * KS;                  // 2 x [D][VS]
-  short* list = reinterpret_cast<short*>(vbuf + 2 * D * VS);
+  char* vbuf = kbuf + 2 * kBK * KS;                  // 2 x V tile
+  short* list = reinterpret_cast<short*>(vbuf + 2 * VT);
   uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
   uint8_t* flags = wbits + kChunk;
   int* counter = reinterpret_cast<int*>(flags + kChunk);
@@ -830,26 +859,30 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
   auto active = [&](int ww, int kt) -> bool {
     return (qtile * kWaves + ww) < P.n_q32 && mask[(mrow0 + ww) * P.n_kt + kt] != 0;
   };
+  RowStage<E, D, kBK> sk;
+  std::conditional_t<kTr, RowStage<E, D, kBK>, ColStage<E, D, kBK>> sv;
+  auto load = [&](int k0) {
+    sk.load(Kh, k0, N);
+    if constexpr (kTr) sv.load(Vh, k0, N);
+    else sv.load(Vh, P.Np, k0);
+  };
+  auto store = [&](int b) {
+    sk.store(kbuf + b * kBK * KS, KS);
+    sv.store(vbuf + b * VT, VS);
+  };
   for (int base = 0; base < P.n_kt; base += kChunk) {
     const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
-    RowStage<E, D, kBK> sk;
-    ColStage<E, D, kBK> sv;
     if (n > 0) {
-      sk.load(Kh, (base + list[0]) * kBK, N);
-      sv.load(Vth, P.Np, (base + list[0]) * kBK);
-      sk.store(kbuf, KS);
-      sv.store(vbuf, VS);
+      load((base + list[0]) * kBK);
+      store(0);
     }
     __syncthreads();
     for (int i = 0; i < n; ++i) {
       const int kt = base + list[i];
-      if (i + 1 < n) {
-        sk.load(Kh, (base + list[i + 1]) * kBK, N);
-        sv.load(Vth, P.Np, (base + list[i + 1]) * kBK);
-      }
+      if (i + 1 < n) load((base + list[i + 1]) * kBK);
       if ((wbits[i] >> w) & 1) {
         const char* kl = kbuf + (i & 1) * kBK * KS;
-        const char* vl = vbuf + (i & 1) * D * VS;
+        const char* vl = vbuf + (i & 1) * VT;
         f32x16 acc[2];
         scores_T<E, D>(acc, kl, KS, qf, lane);
         const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
@@ -878,9 +911,13 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
             const int koff = 32 * kb + 16 * s + 4 * h;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-              const E* vrow = reinterpret_cast<const E*>(vl + (32 * db + c32) * VS);
               Frag<E> vf;
-              ld4x2(vf, vrow + koff, vrow + koff + 8);
+              if constexpr (kTr) {
+                ld_col8(vf, vl, VS, koff, 32 * db, lane);
+              } else {
+                const E* vrow = reinterpret_cast<const E*>(vl + (32 * db + c32) * VS);
+                ld4x2(vf, vrow + koff, vrow + koff + 8);
+              }
               mma(oacc[db], vf, pf);
               if (want_aux) {
                 mma(uacc[db], vf, uf);
@@ -889,10 +926,7 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
             }
           }
       }
-      if (i + 1 < n) {
-        sk.store(kbuf + ((i + 1) & 1) * kBK * KS, KS);
-        sv.store(vbuf + ((i + 1) & 1) * D * VS, VS);
-      }
+      if (i + 1 < n) store((i + 1) & 1);
       __syncthreads();
     }
   }
@@ -941,33 +975,22 @@ __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ in, E* 
   }
 }
 
-// delta_i = dO_i . W_i, one wave per row.
-template <typename E, int D>
-__global__ __launch_bounds__(256) void k_delta(const E* __restrict__ dO, const float* __restrict__ W,
-                                               float* __restrict__ delta, long long rows) {
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  float s = 0.0f;
-#pragma unroll
-  for (int d = lane; d < D; d += 64) s = fmaf((float)dO[row * D + d], W[row * D + d], s);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if (lane == 0) delta[row] = s;
-}
-
 // ---------------------------------------------------------- k_bwd_dq ---
-// Per workgroup (128 queries): dQ = dS K / sqrt(d) over active key tiles,
-// dS^T = U (dP^T - delta) with dP^T = V dO^T, all in the S^T layout.
+// Per workgroup (128 queries): delta_i = dO_i . W_i (written out for the dK/dV
+// kernel), then dQ = dS K / sqrt(d) over active key tiles with
+// dS^T = U (dP^T - delta), dP^T = V dO^T, all in the S^T layout.  bf16 reads
+// the dQ operand down the columns of the staged K tile; fp32 stages K^T too.
 template <typename E, int D, int AK, int NB>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Kt, const float* __restrict__ tau_in,
-    const float* __restrict__ delta_in, const uint8_t* __restrict__ mask, Params P,
-    void* __restrict__ dq) {
+    const float* __restrict__ W, const uint8_t* __restrict__ mask, Params P,
+    float* __restrict__ delta_out, void* __restrict__ dq) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr bool kTr = sizeof(E) == 2;
+  constexpr int KS = row_stride<E, D>();
   constexpr int VS = kBK * (int)sizeof(E) + 16;
+  constexpr int TT = kTr ? 0 : D * VS;              // bytes of one staged K^T tile
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
   int bh, qtile;
@@ -976,13 +999,13 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
   const int iq = wq0 + c32;
   const bool valid = iq < N;
   const size_t hoff = (size_t)bh * N * D;
-  const E* Kth = Kt + (size_t)bh * D * P.Np;
+  const E* Kth = kTr ? nullptr : Kt + (size_t)bh * D * P.Np;
 
   // NB = 2: double-buffered tiles; NB = 1 when two copies exceed the LDS
   char* kbuf = smem;                                 // NB x [64][KS]
   char* vbuf = kbuf + NB * kBK * KS;                 // NB x [64][KS]
-  char* tbuf = vbuf + NB * kBK * KS;                 // NB x [D][VS]
-  short* list = reinterpret_cast<short*>(tbuf + NB * D * VS);
+  char* tbuf = vbuf + NB * kBK * KS;                 // NB x [D][VS] (fp32 only)
+  short* list = reinterpret_cast<short*>(tbuf + NB * TT);
   uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
   uint8_t* flags = wbits + kChunk;
   int* counter = reinterpret_cast<int*>(flags + kChunk);
@@ -991,7 +1014,23 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
   load_qfrags<E, D>(qf, Q + hoff + (size_t)iq * D, valid, h);
   load_qfrags<E, D>(of, dO + hoff + (size_t)iq * D, valid, h);
   const float tau = valid ? tau_in[(size_t)bh * N + iq] : INFINITY;
-  const float dlt = valid ? delta_in[(size_t)bh * N + iq] : 0.0f;
+  // delta_i = dO_i . W_i: each lane half holds half of the row's dO
+  float dlt = 0.0f;
+  if (valid) {
+    const float* wr = W + hoff + (size_t)iq * D;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(wr + 16 * c + 8 * h);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(wr + 16 * c + 8 * h + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dlt = fmaf(frag_get(of[c], j), w0[j], dlt);
+        dlt = fmaf(frag_get(of[c], 4 + j), w1[j], dlt);
+      }
+    }
+  }
+  dlt += __shfl_xor(dlt, 32);
+  if (valid && h == 0) delta_out[(size_t)bh * N + iq] = dlt;
   const bool wave_has_tail = wq0 + kBQ > N;
 
   f32x16 gacc[D / 32];
@@ -1002,32 +1041,33 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
   auto active = [&](int ww, int kt) -> bool {
     return (qtile * kWaves + ww) < P.n_q32 && mask[(mrow0 + ww) * P.n_kt + kt] != 0;
   };
+  RowStage<E, D, kBK> sk, sv;
+  ColStage<E, D, kBK> st;
+  auto load = [&](int k0) {
+    sk.load(K + hoff, k0, N);
+    sv.load(V + hoff, k0, N);
+    if constexpr (!kTr) st.load(Kth, P.Np, k0);
+  };
+  auto store = [&](int b) {
+    sk.store(kbuf + b * kBK * KS, KS);
+    sv.store(vbuf + b * kBK * KS, KS);
+    if constexpr (!kTr) st.store(tbuf + b * TT, VS);
+  };
   for (int base = 0; base < P.n_kt; base += kChunk) {
     const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
-    RowStage<E, D, kBK> sk, sv;
-    ColStage<E, D, kBK> st;
     if (n > 0) {
-      const int k0 = (base + list[0]) * kBK;
-      sk.load(K + hoff, k0, N);
-      sv.load(V + hoff, k0, N);
-      st.load(Kth, P.Np, k0);
-      sk.store(kbuf, KS);
-      sv.store(vbuf, KS);
-      st.store(tbuf, VS);
+      load((base + list[0]) * kBK);
+      store(0);
     }
     __syncthreads();
     for (int i = 0; i < n; ++i) {
       const int kt = base + list[i];
-      if (i + 1 < n) {
-        const int k1 = (base + list[i + 1]) * kBK;
-        sk.load(K + hoff, k1, N);
-        sv.load(V + hoff, k1, N);
-        st.load(Kth, P.Np, k1);
-      }
+      if (i + 1 < n) load((base + list[i + 1]) * kBK);
       if ((wbits[i] >> w) & 1) {
         const int buf = NB == 2 ? (i & 1) : 0;
+        const char* kl = kbuf + buf * kBK * KS;
         f32x16 sacc[2], pacc[2];
-        scores_T<E, D>(sacc, kbuf + buf * kBK * KS, KS, qf, lane);
+        scores_T<E, D>(sacc, kl, KS, qf, lane);
         scores_T<E, D>(pacc, vbuf + buf * kBK * KS, KS, of, lane);
         const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
         if (need) mask_T(sacc, kt * kBK, iq, N, P.causal, h);
@@ -1040,7 +1080,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
             Ent<AK>::pu(t, P.beta, p, u);
             sacc[kb][j] = u * (pacc[kb][j] - dlt);
           }
-        const char* tl = tbuf + buf * D * VS;
+        const char* tl = tbuf + buf * TT;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1052,20 +1092,21 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
             const int koff = 32 * kb + 16 * s + 4 * h;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-              const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
               Frag<E> kf;
-              ld4x2(kf, krow + koff, krow + koff + 8);
+              if constexpr (kTr) {
+                ld_col8(kf, kl, KS, koff, 32 * db, lane);
+              } else {
+                const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
+                ld4x2(kf, krow + koff, krow + koff + 8);
+              }
               mma(gacc[db], kf, sf);
               if constexpr (kNeedsLo<E>) mma(gacc[db], kf, sl);
             }
           }
       }
       if (i + 1 < n) {
-        const int buf = NB == 2 ? ((i + 1) & 1) : 0;
         if (NB == 1) __syncthreads();
-        sk.store(kbuf + buf * kBK * KS, KS);
-        sv.store(vbuf + buf * kBK * KS, KS);
-        st.store(tbuf + buf * D * VS, VS);
+        store(NB == 2 ? ((i + 1) & 1) : 0);
       }
       __syncthreads();
     }
@@ -1091,8 +1132,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
 // -------------------------------------------------------- k_bwd_dkdv ---
 // Per workgroup (128 keys, 32 per wave): dV = P^T dO and dK = dS^T Q / sqrt(d)
 // over the active 32-query blocks of the two mask columns it covers.  Scores
-// are computed as S = Q K^T here (lane = key), so P and dS feed the A operand
-// and the transposed Q / dO tiles the B operand.
+// are computed as S = Q K^T here (lane = key), so P and dS feed the A operand;
+// the B operand runs down the columns of the staged Q / dO tiles (bf16:
+// transposed LDS reads; fp32: staged Q^T / dO^T copies).
 template <typename E, int D, int AK>
 __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
@@ -1100,9 +1142,11 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
     const float* __restrict__ tau_in, const float* __restrict__ delta_in,
     const uint8_t* __restrict__ mask, Params P, void* __restrict__ dk, void* __restrict__ dv) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr bool kTr = sizeof(E) == 2;
+  constexpr int KS = row_stride<E, D>();
   constexpr int TS = kBQ * (int)sizeof(E) + 16;
-  constexpr int STEP = 2 * kBQ * KS + 2 * D * TS + 2 * kBQ * 4;   // one pipeline buffer
+  constexpr int TT = kTr ? 0 : D * TS;               // bytes of one staged transposed tile
+  constexpr int STEP = 2 * kBQ * KS + 2 * TT + 2 * kBQ * 4;   // one pipeline buffer
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
   int bh, ktile;
@@ -1112,10 +1156,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
   const bool kvalid = jk < N;
   const bool wave_keys = kw0 < N;
   const size_t hoff = (size_t)bh * N * D;
-  const E* Qth = Qt + (size_t)bh * D * P.Np;
-  const E* dOth = dOt + (size_t)bh * D * P.Np;
+  const E* Qth = kTr ? nullptr : Qt + (size_t)bh * D * P.Np;
+  const E* dOth = kTr ? nullptr : dOt + (size_t)bh * D * P.Np;
 
-  // buffer b: Q rows | dO rows | Q^T cols | dO^T cols | tau[32] | delta[32]
+  // buffer b: Q rows | dO rows | [Q^T cols | dO^T cols] | tau[32] | delta[32]
   short* list = reinterpret_cast<short*>(smem + 2 * STEP);
   uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
   uint8_t* flags = wbits + kChunk;
@@ -1132,7 +1176,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
     dva[db] = f32x16{};
   }
   const int ktA = (ktile * 128) / kBK, ktB = ktA + 1;
-  const bool hasB = ktB < P.n_kt;
   const size_t mbase = (size_t)bh * P.n_q32;
   // waves 0, 1 cover key tile A (64 keys), waves 2, 3 key tile B
   auto active = [&](int ww, int r) -> bool {
@@ -1141,33 +1184,35 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
     return mask[(mbase + r) * P.n_kt + kt] != 0;
   };
 
-  struct Stage {
-    RowStage<E, D, kBQ> q, o;
-    ColStage<E, D, kBQ> qt, ot;
-    float ta, de;
-  } st;
+  RowStage<E, D, kBQ> sq, so;
+  ColStage<E, D, kBQ> sqt, sot;
+  float sta = 0.0f, sde = 0.0f;
   auto load = [&](int r) {
     const int qb0 = r * kBQ;
-    st.q.load(Q + hoff, qb0, N);
-    st.o.load(dO + hoff, qb0, N);
-    st.qt.load(Qth, P.Np, qb0);
-    st.ot.load(dOth, P.Np, qb0);
+    sq.load(Q + hoff, qb0, N);
+    so.load(dO + hoff, qb0, N);
+    if constexpr (!kTr) {
+      sqt.load(Qth, P.Np, qb0);
+      sot.load(dOth, P.Np, qb0);
+    }
     if (threadIdx.x < kBQ) {
       const int qi = qb0 + threadIdx.x;
-      st.ta = qi < N ? tau_in[(size_t)bh * N + qi] : INFINITY;
-      st.de = qi < N ? delta_in[(size_t)bh * N + qi] : 0.0f;
+      sta = qi < N ? tau_in[(size_t)bh * N + qi] : INFINITY;
+      sde = qi < N ? delta_in[(size_t)bh * N + qi] : 0.0f;
     }
   };
   auto store = [&](int b) {
     char* p = smem + b * STEP;
-    st.q.store(p, KS);
-    st.o.store(p + kBQ * KS, KS);
-    st.qt.store(p + 2 * kBQ * KS, TS);
-    st.ot.store(p + 2 * kBQ * KS + D * TS, TS);
+    sq.store(p, KS);
+    so.store(p + kBQ * KS, KS);
+    if constexpr (!kTr) {
+      sqt.store(p + 2 * kBQ * KS, TS);
+      sot.store(p + 2 * kBQ * KS + TT, TS);
+    }
     if (threadIdx.x < kBQ) {
-      float* f = reinterpret_cast<float*>(p + 2 * kBQ * KS + 2 * D * TS);
-      f[threadIdx.x] = st.ta;
-      f[kBQ + threadIdx.x] = st.de;
+      float* f = reinterpret_cast<float*>(p + 2 * kBQ * KS + 2 * TT);
+      f[threadIdx.x] = sta;
+      f[kBQ + threadIdx.x] = sde;
     }
   };
 
@@ -1187,8 +1232,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
         const char* qtl = p;
         const char* otl = p + kBQ * KS;
         const char* qttl = p + 2 * kBQ * KS;
-        const char* ottl = qttl + D * TS;
-        const float* taus = reinterpret_cast<const float*>(ottl + D * TS);
+        const char* ottl = qttl + TT;
+        const float* taus = reinterpret_cast<const float*>(p + 2 * kBQ * KS + 2 * TT);
         const float* dels = taus + kBQ;
         // S = Q K^T and dP = dO V^T: rows = the 32 queries, column = this lane's key
         f32x16 sacc = f32x16{}, pacc = f32x16{};
@@ -1204,9 +1249,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
         for (int j = 0; j < 16; ++j) {
           const int qr = acc_row(j, h);
           const int qi = qb0 + qr;
-          float s = sacc[j];
-          if (!kvalid || qi >= N || (P.causal && jk > qi)) s = -INFINITY;
-          const float t = clamp01(fmaf(s, P.scale, -taus[qr]));
+          float sv = sacc[j];
+          if (!kvalid || qi >= N || (P.causal && jk > qi)) sv = -INFINITY;
+          const float t = clamp01(fmaf(sv, P.scale, -taus[qr]));
           float pp, u;
           Ent<AK>::pu(t, P.beta, pp, u);
           sacc[j] = pp;
@@ -1220,11 +1265,16 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
           const int qoff = 16 * s + 4 * h;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
-            const E* orow = reinterpret_cast<const E*>(ottl + (32 * db + c32) * TS);
-            const E* qrow = reinterpret_cast<const E*>(qttl + (32 * db + c32) * TS);
             Frag<E> ob, qb;
-            ld4x2(ob, orow + qoff, orow + qoff + 8);
-            ld4x2(qb, qrow + qoff, qrow + qoff + 8);
+            if constexpr (kTr) {
+              ld_col8(ob, otl, KS, qoff, 32 * db, lane);
+              ld_col8(qb, qtl, KS, qoff, 32 * db, lane);
+            } else {
+              const E* orow = reinterpret_cast<const E*>(ottl + (32 * db + c32) * TS);
+              const E* qrow = reinterpret_cast<const E*>(qttl + (32 * db + c32) * TS);
+              ld4x2(ob, orow + qoff, orow + qoff + 8);
+              ld4x2(qb, qrow + qoff, qrow + qoff + 8);
+            }
             mma(dva[db], pf, ob);
             mma(dka[db], sf, qb);
           }
@@ -1300,17 +1350,22 @@ int check_alpha(float alpha) {
   return EA_OK;
 }
 
-size_t transposed_bytes(const Shape& s) { return align_up((size_t)s.BH * s.d * s.Np * s.esz, 256); }
+// Transposed copies are needed only for fp32 inputs: bf16 tiles are read down
+// their columns with ds_read_b64_tr_b16 instead.
+size_t transposed_bytes(const Shape& s) {
+  return s.esz == 4 ? align_up((size_t)s.BH * s.d * s.Np * s.esz, 256) : 0;
+}
 size_t row_bytes(const Shape& s) { return align_up((size_t)s.BH * s.N * sizeof(float), 256); }
 size_t tilemax_bytes(const Shape& s) {
   return align_up((size_t)s.BH * s.n_q32 * s.n_kt * sizeof(float), 256);
 }
 
 size_t workspace_bytes(const Shape& s) {
-  // forward: V^T | row maxima | tile maxima;  backward: K^T | Q^T | dO^T | delta
+  // forward: [V^T] | row maxima | tile maxima;  backward: [K^T | Q^T | dO^T] | delta
   const size_t fwd = transposed_bytes(s) + row_bytes(s) + tilemax_bytes(s);
   const size_t bwd = 3 * transposed_bytes(s) + row_bytes(s);
-  return bwd > fwd ? bwd : fwd;
+  const size_t ws = bwd > fwd ? bwd : fwd;
+  return ws > 256 ? ws : 256;
 }
 
 int alpha_kind(float alpha) {
@@ -1367,6 +1422,7 @@ template <typename E, int D, int AK>
 int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const void* v, void* out,
                float* tau, uint8_t* mask, float* aux, uint8_t* iters, void* ws, hipStream_t st,
                StageTimer tm) {
+  constexpr bool kTr = sizeof(E) == 2;
   const E* Q = static_cast<const E*>(q);
   const E* K = static_cast<const E*>(k);
   const E* V = static_cast<const E*>(v);
@@ -1378,10 +1434,11 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   int rc;
 
   tm.begin(EA_STAGE_FWD_PREP);
-  hipLaunchKernelGGL(k_transpose<E>, dim3(s.Np / 64, D / 64, s.BH), dim3(256), 0, st, V, Vt, s.N, D, s.Np);
+  if constexpr (!kTr)
+    hipLaunchKernelGGL(k_transpose<E>, dim3(s.Np / 64, D / 64, s.BH), dim3(256), 0, st, V, Vt, s.N, D, s.Np);
   tm.end(EA_STAGE_FWD_PREP);
 
-  constexpr int KS = D * (int)sizeof(E) + 16;
+  constexpr int KS = row_stride<E, D>();
   const size_t rm_lds = (size_t)2 * kBK * KS;
   auto krm = k_rowmax<E, D>;
   if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
@@ -1398,12 +1455,12 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   hipLaunchKernelGGL(ktau, g, dim3(kThreads), tau_lds, st, Q, K, rowmax, tilemax, P, tau, mask, iters);
   tm.end(EA_STAGE_TAU);
 
-  constexpr int VS = kBK * (int)sizeof(E) + 16;
-  const size_t pv_lds = (size_t)2 * kBK * KS + (size_t)2 * D * VS + 4 * kChunk + 16;
+  constexpr int VT = kTr ? kBK * KS : D * (kBK * (int)sizeof(E) + 16);
+  const size_t pv_lds = (size_t)2 * kBK * KS + (size_t)2 * VT + 4 * kChunk + 16;
   auto kpv = k_pv<E, D, AK>;
   if ((rc = set_lds(kpv, pv_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_PV);
-  hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, Vt, tau, mask, P, out, aux);
+  hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, kTr ? V : Vt, tau, mask, P, out, aux);
   tm.end(EA_STAGE_PV);
   return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }
@@ -1412,6 +1469,7 @@ template <typename E, int D, int AK>
 int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const void* v,
                const void* dout, const float* tau, const uint8_t* mask, const float* aux, void* dq,
                void* dk, void* dv, void* ws, hipStream_t st, StageTimer tm) {
+  constexpr bool kTr = sizeof(E) == 2;
   const E* Q = static_cast<const E*>(q);
   const E* K = static_cast<const E*>(k);
   const E* V = static_cast<const E*>(v);
@@ -1424,29 +1482,28 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
   E* dOt = reinterpret_cast<E*>(w + 2 * tb);
   float* delta = reinterpret_cast<float*>(w + 3 * tb);
   int rc;
-  const dim3 tg(s.Np / 64, D / 64, s.BH);
   tm.begin(EA_STAGE_BWD_PREP);
-  hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, K, Kt, s.N, D, s.Np);
-  hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, Q, Qt, s.N, D, s.Np);
-  hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, dO, dOt, s.N, D, s.Np);
-  const long long rows = (long long)s.BH * s.N;
-  hipLaunchKernelGGL((k_delta<E, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, dO, aux,
-                     delta, rows);
+  if constexpr (!kTr) {
+    const dim3 tg(s.Np / 64, D / 64, s.BH);
+    hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, K, Kt, s.N, D, s.Np);
+    hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, Q, Qt, s.N, D, s.Np);
+    hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, dO, dOt, s.N, D, s.Np);
+  }
   tm.end(EA_STAGE_BWD_PREP);
 
-  constexpr int KS = D * (int)sizeof(E) + 16;
-  constexpr int VS = kBK * (int)sizeof(E) + 16;
-  constexpr int TS = kBQ * (int)sizeof(E) + 16;
-  constexpr int NB = (4 * kBK * KS + 2 * D * VS + 4 * kChunk + 16) <= 160 * 1024 ? 2 : 1;
-  const size_t dq_lds = (size_t)NB * (2 * kBK * KS + D * VS) + 4 * kChunk + 16;
+  constexpr int KS = row_stride<E, D>();
+  constexpr int TT = kTr ? 0 : D * (kBK * (int)sizeof(E) + 16);
+  constexpr int NB = (2 * (2 * kBK * KS + TT) + 4 * kChunk + 16) <= 160 * 1024 ? 2 : 1;
+  const size_t dq_lds = (size_t)NB * (2 * kBK * KS + TT) + 4 * kChunk + 16;
   auto kdq = k_bwd_dq<E, D, AK, NB>;
   if ((rc = set_lds(kdq, dq_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_DQ);
-  hipLaunchKernelGGL(kdq, dim3(s.n_qt128 * s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO, Kt, tau,
-                     delta, mask, P, dq);
+  hipLaunchKernelGGL(kdq, dim3(s.n_qt128 * s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO, Kt, tau, aux,
+                     mask, P, delta, dq);
   tm.end(EA_STAGE_DQ);
 
-  const size_t kv_lds = (size_t)2 * (2 * kBQ * KS + 2 * D * TS + 2 * kBQ * 4) + 4 * kChunk + 16;
+  constexpr int TTq = kTr ? 0 : D * (kBQ * (int)sizeof(E) + 16);
+  const size_t kv_lds = (size_t)2 * (2 * kBQ * KS + 2 * TTq + 2 * kBQ * 4) + 4 * kChunk + 16;
   auto kkv = k_bwd_dkdv<E, D, AK>;
   if ((rc = set_lds(kkv, kv_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_DKDV);

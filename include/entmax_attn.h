@@ -90,18 +90,18 @@ typedef struct {
 } ea_desc;
 
 /* Stages, for the timing hook. */
-#define EA_STAGE_FWD_PREP  0   /* forward: V^T copy */
+#define EA_STAGE_FWD_PREP  0   /* forward: V^T copy (fp32 inputs only) */
 #define EA_STAGE_ROWMAX    1   /* forward: the full score sweep (row and tile maxima) */
 #define EA_STAGE_TAU       2   /* forward: histogram and Halley sweeps over candidate tiles, block mask */
 #define EA_STAGE_PV        3   /* forward: O = P V and W = U V / sum U over active tiles */
-#define EA_STAGE_BWD_PREP  4   /* backward: K^T, Q^T, dO^T copies and delta */
-#define EA_STAGE_DQ        5   /* backward: dQ over active tiles */
+#define EA_STAGE_BWD_PREP  4   /* backward: K^T, Q^T, dO^T copies (fp32 inputs only) */
+#define EA_STAGE_DQ        5   /* backward: delta = dO . W, then dQ over active tiles */
 #define EA_STAGE_DKDV      6   /* backward: dK, dV over active tiles */
 #define EA_NUM_STAGES      7
 
-/* Bytes of device workspace both entry points need for `desc`: transposed
- * copies of V (forward) or of K, Q, dO (backward), one float per row, and
- * (forward) one float per block_mask tile.  O(B*H*N*d + B*H*n_qt*n_kt); no
+/* Bytes of device workspace both entry points need for `desc`: one float per
+ * row, (forward) one float per block_mask tile, and for fp32 inputs transposed
+ * copies of V (forward) or of K, Q, dO (backward).  O(B*H*N*d + B*H*n_qt*n_kt); no
  * N^2-element buffer.  Returns 0 for an invalid desc. */
 size_t entmax_attn_workspace_bytes(const ea_desc* desc);
 
