@@ -9,7 +9,6 @@ from .binding import (  # noqa: F401
     EntmaxAttnError,
     EaDesc,
     entmax_attention,
-    entmax_attn_aux_bytes,
     entmax_attn_bwd,
     entmax_attn_fwd,
     entmax_attn_mask_dims,

@@ -24,7 +24,6 @@ TAU_MODES = {"hist": EA_TAU_HIST_HALLEY, "halley": EA_TAU_HALLEY_BISECT, "bisect
 
 EXPORTED = (
     "entmax_attn_workspace_bytes",
-    "entmax_attn_aux_bytes",
     "entmax_attn_mask_dims",
     "entmax_attn_fwd",
     "entmax_attn_bwd",
@@ -64,14 +63,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     dp = ctypes.POINTER(EaDesc)
     lib.entmax_attn_workspace_bytes.argtypes = [dp]
     lib.entmax_attn_workspace_bytes.restype = sz
-    lib.entmax_attn_aux_bytes.argtypes = [dp]
-    lib.entmax_attn_aux_bytes.restype = sz
     ip = ctypes.POINTER(ctypes.c_int)
     lib.entmax_attn_mask_dims.argtypes = [dp, ip, ip, ip, ip]
     lib.entmax_attn_mask_dims.restype = i32
-    lib.entmax_attn_fwd.argtypes = [vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, dp, vp, sz, vp]
+    lib.entmax_attn_fwd.argtypes = [vp, vp, vp, f32, i32, vp, vp, vp, vp, dp, vp, sz, vp]
     lib.entmax_attn_fwd.restype = i32
-    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, vp, dp, vp, sz, vp]
+    lib.entmax_attn_bwd.argtypes = [vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, dp, vp, sz, vp]
     lib.entmax_attn_bwd.restype = i32
     lib.entmax_attn_strerror.argtypes = [i32]
     lib.entmax_attn_strerror.restype = ctypes.c_char_p
@@ -114,10 +111,6 @@ def entmax_attn_workspace_bytes(desc: EaDesc) -> int:
     return int(load_library().entmax_attn_workspace_bytes(ctypes.byref(desc)))
 
 
-def entmax_attn_aux_bytes(desc: EaDesc) -> int:
-    return int(load_library().entmax_attn_aux_bytes(ctypes.byref(desc)))
-
-
 def entmax_attn_mask_dims(desc: EaDesc):
     vals = [ctypes.c_int() for _ in range(4)]
     st = load_library().entmax_attn_mask_dims(ctypes.byref(desc), *[ctypes.byref(v) for v in vals])
@@ -126,21 +119,21 @@ def entmax_attn_mask_dims(desc: EaDesc):
     return tuple(v.value for v in vals)
 
 
-def entmax_attn_fwd(q, k, v, alpha, causal, out, tau, block_mask, aux, tau_iters, desc, ws,
+def entmax_attn_fwd(q, k, v, alpha, causal, out, tau, block_mask, tau_iters, desc, ws,
                     stream=None) -> None:
     st = load_library().entmax_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), float(alpha), int(bool(causal)), _ptr(out), _ptr(tau),
-        _ptr(block_mask), _ptr(aux), _ptr(tau_iters), ctypes.byref(desc), _ptr(ws),
+        _ptr(block_mask), _ptr(tau_iters), ctypes.byref(desc), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     if st != EA_OK:
         raise EntmaxAttnError(st, "entmax_attn_fwd")
 
 
-def entmax_attn_bwd(q, k, v, alpha, causal, dout, tau, block_mask, aux, dq, dk, dv, desc, ws,
+def entmax_attn_bwd(q, k, v, alpha, causal, dout, tau, block_mask, dq, dk, dv, desc, ws,
                     stream=None) -> None:
     st = load_library().entmax_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), float(alpha), int(bool(causal)), _ptr(dout), _ptr(tau),
-        _ptr(block_mask), _ptr(aux), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.byref(desc), _ptr(ws),
+        _ptr(block_mask), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.byref(desc), _ptr(ws),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     if st != EA_OK:
         raise EntmaxAttnError(st, "entmax_attn_bwd")
@@ -159,7 +152,6 @@ class Buffers:
         self.out = torch.empty(B, H, N, d, dtype=out_dtype, device=dev)
         self.tau = torch.empty(B, H, N, dtype=torch.float32, device=dev)
         self.mask = torch.empty(B, H, n_qt, n_kt, dtype=torch.uint8, device=dev)
-        self.aux = torch.empty(B, H, N, d, dtype=torch.float32, device=dev)
         self.iters = torch.empty(B, H, N, dtype=torch.uint8, device=dev)
         ws = entmax_attn_workspace_bytes(self.desc)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
@@ -168,12 +160,12 @@ class Buffers:
         self.dv = torch.empty_like(self.dq)
 
     def forward(self, q, k, v, alpha, causal, stream=None):
-        entmax_attn_fwd(q, k, v, alpha, causal, self.out, self.tau, self.mask, self.aux, self.iters,
+        entmax_attn_fwd(q, k, v, alpha, causal, self.out, self.tau, self.mask, self.iters,
                         self.desc, self.ws, stream)
         return self.out
 
     def backward(self, q, k, v, dout, alpha, causal, stream=None):
-        entmax_attn_bwd(q, k, v, alpha, causal, dout, self.tau, self.mask, self.aux, self.dq,
+        entmax_attn_bwd(q, k, v, alpha, causal, dout, self.tau, self.mask, self.dq,
                         self.dk, self.dv, self.desc, self.ws, stream)
         return self.dq, self.dk, self.dv
 

@@ -807,17 +807,15 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
 }
 
 // -------------------------------------------------------------- k_pv ---
-// Per workgroup (128 queries): O = P V and W = (U V) / sum(U) over the
-// active key tiles of the block mask.  U = t^(beta-1) is the entmax
-// Jacobian weight; W carries delta_i = dO_i . W_i to the backward.
-// bf16: V tiles are staged as rows and read down their columns with
+// Per workgroup (128 queries): O = P V over the active key tiles of the
+// block mask.  bf16: V tiles are staged as rows and read down their columns with
 // transposed LDS reads; fp32: Vsrc is a V^T copy [BH][D][Np].
 template <typename E, int D, int AK>
 __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const E* __restrict__ K,
                                                  const E* __restrict__ Vsrc,
                                                  const float* __restrict__ tau_in,
                                                  const uint8_t* __restrict__ mask, Params P,
-                                                 void* __restrict__ out, float* __restrict__ aux) {
+                                                 void* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool kTr = sizeof(E) == 2;
   constexpr int KS = row_stride<E, D>();
@@ -845,15 +843,10 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
   load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
   const float tau = valid ? tau_in[(size_t)bh * N + iq] : INFINITY;
   const bool wave_has_tail = wq0 + kBQ > N;
-  const bool want_aux = aux != nullptr;
 
-  f32x16 oacc[D / 32], uacc[D / 32];
+  f32x16 oacc[D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    oacc[db] = f32x16{};
-    uacc[db] = f32x16{};
-  }
-  float usum = 0.0f;
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
   const size_t mrow0 = (size_t)bh * P.n_q32 + (size_t)qtile * kWaves;
   auto active = [&](int ww, int kt) -> bool {
@@ -887,7 +880,6 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
         scores_T<E, D>(acc, kl, KS, qf, lane);
         const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
         if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
-        f32x16 uu[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -896,18 +888,13 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
             float p, u;
             Ent<AK>::pu(t, P.beta, p, u);
             acc[kb][j] = p;
-            uu[kb][j] = u;
-            usum += u;
           }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
-            Frag<E> pf, uf, ul;
+            Frag<E> pf;
             from_acc(pf, acc[kb], 8 * s);
-            // U V feeds delta = dO . (U V) / sum(U) in the backward, where it is
-            // subtracted from dP: keep U to ~2^-17 with a hi/lo pair.
-            split_acc(uf, ul, uu[kb], 8 * s);
             const int koff = 32 * kb + 16 * s + 4 * h;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
@@ -919,10 +906,6 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
                 ld4x2(vf, vrow + koff, vrow + koff + 8);
               }
               mma(oacc[db], vf, pf);
-              if (want_aux) {
-                mma(uacc[db], vf, uf);
-                if constexpr (kNeedsLo<E>) mma(uacc[db], vf, ul);
-              }
             }
           }
       }
@@ -930,9 +913,7 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
       __syncthreads();
     }
   }
-  usum += __shfl_xor(usum, 32);
   if (!valid) return;
-  const float inv_u = usum > 0.0f ? 1.0f / usum : 0.0f;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -945,11 +926,6 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
         *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + off) = ob;
       } else {
         *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = o;
-      }
-      if (want_aux) {
-        const f32x4 a = f32x4{uacc[db][4 * g] * inv_u, uacc[db][4 * g + 1] * inv_u,
-                              uacc[db][4 * g + 2] * inv_u, uacc[db][4 * g + 3] * inv_u};
-        *reinterpret_cast<f32x4*>(aux + off) = a;
       }
     }
 }
@@ -976,16 +952,18 @@ __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ in, E* 
 }
 
 // ---------------------------------------------------------- k_bwd_dq ---
-// Per workgroup (128 queries): delta_i = dO_i . W_i (written out for the dK/dV
-// kernel), then dQ = dS K / sqrt(d) over active key tiles with
-// dS^T = U (dP^T - delta), dP^T = V dO^T, all in the S^T layout.  bf16 reads
-// the dQ operand down the columns of the staged K tile; fp32 stages K^T too.
+// Per workgroup (128 queries), two passes over the active key tiles:
+//  1. delta_i = sum_j u_ij dP_ij / sum_j u_ij (fp32, exact weights), written
+//     out for the dK/dV kernel;
+//  2. dQ = dS K / sqrt(d) with dS^T = U (dP^T - delta),
+// where dP^T = V dO^T, all in the S^T layout.  bf16 reads the dQ operand
+// down the columns of the staged K tile; fp32 stages K^T too.
 template <typename E, int D, int AK, int NB>
 __global__ __launch_bounds__(kThreads) void k_bwd_dq(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Kt, const float* __restrict__ tau_in,
-    const float* __restrict__ W, const uint8_t* __restrict__ mask, Params P,
-    float* __restrict__ delta_out, void* __restrict__ dq) {
+    const uint8_t* __restrict__ mask, Params P, float* __restrict__ delta_out,
+    void* __restrict__ dq) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool kTr = sizeof(E) == 2;
   constexpr int KS = row_stride<E, D>();
@@ -1014,28 +992,12 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
   load_qfrags<E, D>(qf, Q + hoff + (size_t)iq * D, valid, h);
   load_qfrags<E, D>(of, dO + hoff + (size_t)iq * D, valid, h);
   const float tau = valid ? tau_in[(size_t)bh * N + iq] : INFINITY;
-  // delta_i = dO_i . W_i: each lane half holds half of the row's dO
-  float dlt = 0.0f;
-  if (valid) {
-    const float* wr = W + hoff + (size_t)iq * D;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(wr + 16 * c + 8 * h);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(wr + 16 * c + 8 * h + 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dlt = fmaf(frag_get(of[c], j), w0[j], dlt);
-        dlt = fmaf(frag_get(of[c], 4 + j), w1[j], dlt);
-      }
-    }
-  }
-  dlt += __shfl_xor(dlt, 32);
-  if (valid && h == 0) delta_out[(size_t)bh * N + iq] = dlt;
   const bool wave_has_tail = wq0 + kBQ > N;
 
   f32x16 gacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) gacc[db] = f32x16{};
+  float num = 0.0f, den = 0.0f, dlt = 0.0f;
 
   const size_t mrow0 = (size_t)bh * P.n_q32 + (size_t)qtile * kWaves;
   auto active = [&](int ww, int kt) -> bool {
@@ -1043,72 +1005,98 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
   };
   RowStage<E, D, kBK> sk, sv;
   ColStage<E, D, kBK> st;
-  auto load = [&](int k0) {
-    sk.load(K + hoff, k0, N);
-    sv.load(V + hoff, k0, N);
-    if constexpr (!kTr) st.load(Kth, P.Np, k0);
-  };
-  auto store = [&](int b) {
-    sk.store(kbuf + b * kBK * KS, KS);
-    sv.store(vbuf + b * kBK * KS, KS);
-    if constexpr (!kTr) st.store(tbuf + b * TT, VS);
-  };
-  for (int base = 0; base < P.n_kt; base += kChunk) {
-    const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
-    if (n > 0) {
-      load((base + list[0]) * kBK);
-      store(0);
-    }
-    __syncthreads();
-    for (int i = 0; i < n; ++i) {
-      const int kt = base + list[i];
-      if (i + 1 < n) load((base + list[i + 1]) * kBK);
-      if ((wbits[i] >> w) & 1) {
-        const int buf = NB == 2 ? (i & 1) : 0;
-        const char* kl = kbuf + buf * kBK * KS;
-        f32x16 sacc[2], pacc[2];
-        scores_T<E, D>(sacc, kl, KS, qf, lane);
-        scores_T<E, D>(pacc, vbuf + buf * kBK * KS, KS, of, lane);
-        const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
-        if (need) mask_T(sacc, kt * kBK, iq, N, P.causal, h);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
-            float p, u;
-            Ent<AK>::pu(t, P.beta, p, u);
-            sacc[kb][j] = u * (pacc[kb][j] - dlt);
-          }
-        const char* tl = tbuf + buf * TT;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            // dQ = sum_j dS_ij k_j cancels strongly when the supporting keys are
-            // nearly parallel (sum_j dS_ij = 0): dS goes in as a hi/lo bf16 pair.
-            Frag<E> sf, sl;
-            split_acc(sf, sl, sacc[kb], 8 * s);
-            const int koff = 32 * kb + 16 * s + 4 * h;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              Frag<E> kf;
-              if constexpr (kTr) {
-                ld_col8(kf, kl, KS, koff, 32 * db, lane);
-              } else {
-                const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
-                ld4x2(kf, krow + koff, krow + koff + 8);
-              }
-              mma(gacc[db], kf, sf);
-              if constexpr (kNeedsLo<E>) mma(gacc[db], kf, sl);
-            }
-          }
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool need_kt = !kTr && pass == 1;
+    auto load = [&](int k0) {
+      sk.load(K + hoff, k0, N);
+      sv.load(V + hoff, k0, N);
+      if constexpr (!kTr) {
+        if (need_kt) st.load(Kth, P.Np, k0);
       }
-      if (i + 1 < n) {
-        if (NB == 1) __syncthreads();
-        store(NB == 2 ? ((i + 1) & 1) : 0);
+    };
+    auto store = [&](int b) {
+      sk.store(kbuf + b * kBK * KS, KS);
+      sv.store(vbuf + b * kBK * KS, KS);
+      if constexpr (!kTr) {
+        if (need_kt) st.store(tbuf + b * TT, VS);
+      }
+    };
+    for (int base = 0; base < P.n_kt; base += kChunk) {
+      const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
+      if (n > 0) {
+        load((base + list[0]) * kBK);
+        store(0);
       }
       __syncthreads();
+      for (int i = 0; i < n; ++i) {
+        const int kt = base + list[i];
+        if (i + 1 < n) load((base + list[i + 1]) * kBK);
+        if ((wbits[i] >> w) & 1) {
+          const int buf = NB == 2 ? (i & 1) : 0;
+          const char* kl = kbuf + buf * kBK * KS;
+          f32x16 sacc[2], pacc[2];
+          scores_T<E, D>(sacc, kl, KS, qf, lane);
+          scores_T<E, D>(pacc, vbuf + buf * kBK * KS, KS, of, lane);
+          const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
+          if (need) mask_T(sacc, kt * kBK, iq, N, P.causal, h);
+          if (pass == 0) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int j = 0; j < 16; ++j) {
+                const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
+                float p, u;
+                Ent<AK>::pu(t, P.beta, p, u);
+                num = fmaf(u, pacc[kb][j], num);
+                den += u;
+              }
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int j = 0; j < 16; ++j) {
+                const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
+                float p, u;
+                Ent<AK>::pu(t, P.beta, p, u);
+                sacc[kb][j] = u * (pacc[kb][j] - dlt);
+              }
+            const char* tl = tbuf + buf * TT;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int s = 0; s < 2; ++s) {
+                // dQ = sum_j dS_ij k_j cancels strongly when the supporting keys are
+                // nearly parallel (sum_j dS_ij = 0): dS goes in as a hi/lo bf16 pair.
+                Frag<E> sf, sl;
+                split_acc(sf, sl, sacc[kb], 8 * s);
+                const int koff = 32 * kb + 16 * s + 4 * h;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                  Frag<E> kf;
+                  if constexpr (kTr) {
+                    ld_col8(kf, kl, KS, koff, 32 * db, lane);
+                  } else {
+                    const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
+                    ld4x2(kf, krow + koff, krow + koff + 8);
+                  }
+                  mma(gacc[db], kf, sf);
+                  if constexpr (kNeedsLo<E>) mma(gacc[db], kf, sl);
+                }
+              }
+          }
+        }
+        if (i + 1 < n) {
+          if (NB == 1) __syncthreads();
+          store(NB == 2 ? ((i + 1) & 1) : 0);
+        }
+        __syncthreads();
+      }
+    }
+    if (pass == 0) {
+      num += __shfl_xor(num, 32);
+      den += __shfl_xor(den, 32);
+      dlt = den > 0.0f ? num / den : 0.0f;
+      if (valid && h == 0) delta_out[(size_t)bh * N + iq] = dlt;
     }
   }
   if (!valid) return;
@@ -1420,8 +1408,7 @@ int set_lds(F* fn, size_t bytes) {
 
 template <typename E, int D, int AK>
 int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const void* v, void* out,
-               float* tau, uint8_t* mask, float* aux, uint8_t* iters, void* ws, hipStream_t st,
-               StageTimer tm) {
+               float* tau, uint8_t* mask, uint8_t* iters, void* ws, hipStream_t st, StageTimer tm) {
   constexpr bool kTr = sizeof(E) == 2;
   const E* Q = static_cast<const E*>(q);
   const E* K = static_cast<const E*>(k);
@@ -1460,15 +1447,15 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   auto kpv = k_pv<E, D, AK>;
   if ((rc = set_lds(kpv, pv_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_PV);
-  hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, kTr ? V : Vt, tau, mask, P, out, aux);
+  hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, kTr ? V : Vt, tau, mask, P, out);
   tm.end(EA_STAGE_PV);
   return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }
 
 template <typename E, int D, int AK>
 int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const void* v,
-               const void* dout, const float* tau, const uint8_t* mask, const float* aux, void* dq,
-               void* dk, void* dv, void* ws, hipStream_t st, StageTimer tm) {
+               const void* dout, const float* tau, const uint8_t* mask, void* dq, void* dk, void* dv,
+               void* ws, hipStream_t st, StageTimer tm) {
   constexpr bool kTr = sizeof(E) == 2;
   const E* Q = static_cast<const E*>(q);
   const E* K = static_cast<const E*>(k);
@@ -1498,8 +1485,8 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
   auto kdq = k_bwd_dq<E, D, AK, NB>;
   if ((rc = set_lds(kdq, dq_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_DQ);
-  hipLaunchKernelGGL(kdq, dim3(s.n_qt128 * s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO, Kt, tau, aux,
-                     mask, P, delta, dq);
+  hipLaunchKernelGGL(kdq, dim3(s.n_qt128 * s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO, Kt, tau, mask,
+                     P, delta, dq);
   tm.end(EA_STAGE_DQ);
 
   constexpr int TTq = kTr ? 0 : D * (kBQ * (int)sizeof(E) + 16);
@@ -1561,12 +1548,6 @@ size_t entmax_attn_workspace_bytes(const ea_desc* desc) {
   return workspace_bytes(s);
 }
 
-size_t entmax_attn_aux_bytes(const ea_desc* desc) {
-  Shape s;
-  if (check_desc(desc, &s) != EA_OK) return 0;
-  return (size_t)s.BH * s.N * s.d * sizeof(float);
-}
-
 int entmax_attn_mask_dims(const ea_desc* desc, int* n_qt, int* n_kt, int* bm, int* bn) {
   Shape s;
   int st = check_desc(desc, &s);
@@ -1579,8 +1560,8 @@ int entmax_attn_mask_dims(const ea_desc* desc, int* n_qt, int* n_kt, int* bm, in
 }
 
 int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, int causal, void* out,
-                    float* tau, uint8_t* block_mask, void* aux, uint8_t* tau_iters,
-                    const ea_desc* desc, void* ws, size_t ws_bytes, void* stream) {
+                    float* tau, uint8_t* block_mask, uint8_t* tau_iters, const ea_desc* desc, void* ws,
+                    size_t ws_bytes, void* stream) {
   Shape s;
   int st = check_desc(desc, &s);
   if (st != EA_OK) return st;
@@ -1589,37 +1570,35 @@ int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, in
   if (s.N > 0) {
     if (!q || !k || !v || !out || !tau || !block_mask || !ws) return EA_ERR_NULL;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(tau) ||
-        misaligned(aux) || misaligned(ws))
+        misaligned(ws))
       return EA_ERR_ALIGN;
     if (ws_bytes < workspace_bytes(s)) return EA_ERR_WORKSPACE;
   }
   Params P = make_params(desc, s, alpha, causal);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  EA_DISPATCH(launch_fwd, s, P, q, k, v, out, tau, block_mask, static_cast<float*>(aux), tau_iters, ws,
-              hs, StageTimer{desc->events, hs});
+  EA_DISPATCH(launch_fwd, s, P, q, k, v, out, tau, block_mask, tau_iters, ws, hs,
+              StageTimer{desc->events, hs});
 }
 
 int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, int causal,
-                    const void* dout, const float* tau, const uint8_t* block_mask, const void* aux,
-                    void* dq, void* dk, void* dv, const ea_desc* desc, void* ws, size_t ws_bytes,
-                    void* stream) {
+                    const void* dout, const float* tau, const uint8_t* block_mask, void* dq, void* dk,
+                    void* dv, const ea_desc* desc, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   int st = check_desc(desc, &s);
   if (st != EA_OK) return st;
   if ((st = check_alpha(alpha)) != EA_OK) return st;
   if (causal != 0 && causal != 1) return EA_ERR_UNSUPPORTED;
   if (s.N > 0) {
-    if (!q || !k || !v || !dout || !tau || !block_mask || !aux || !dq || !dk || !dv || !ws)
-      return EA_ERR_NULL;
+    if (!q || !k || !v || !dout || !tau || !block_mask || !dq || !dk || !dv || !ws) return EA_ERR_NULL;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(dout) || misaligned(tau) ||
-        misaligned(aux) || misaligned(dq) || misaligned(dk) || misaligned(dv) || misaligned(ws))
+        misaligned(dq) || misaligned(dk) || misaligned(dv) || misaligned(ws))
       return EA_ERR_ALIGN;
     if (ws_bytes < workspace_bytes(s)) return EA_ERR_WORKSPACE;
   }
   Params P = make_params(desc, s, alpha, causal);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  EA_DISPATCH(launch_bwd, s, P, q, k, v, dout, tau, block_mask, static_cast<const float*>(aux), dq, dk,
-              dv, ws, hs, StageTimer{desc->events, hs});
+  EA_DISPATCH(launch_bwd, s, P, q, k, v, dout, tau, block_mask, dq, dk, dv, ws, hs,
+              StageTimer{desc->events, hs});
 }
 
 const char* entmax_attn_strerror(int status) {

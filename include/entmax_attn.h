@@ -93,9 +93,9 @@ typedef struct {
 #define EA_STAGE_FWD_PREP  0   /* forward: V^T copy (fp32 inputs only) */
 #define EA_STAGE_ROWMAX    1   /* forward: the full score sweep (row and tile maxima) */
 #define EA_STAGE_TAU       2   /* forward: histogram and Halley sweeps over candidate tiles, block mask */
-#define EA_STAGE_PV        3   /* forward: O = P V and W = U V / sum U over active tiles */
+#define EA_STAGE_PV        3   /* forward: O = P V over active tiles */
 #define EA_STAGE_BWD_PREP  4   /* backward: K^T, Q^T, dO^T copies (fp32 inputs only) */
-#define EA_STAGE_DQ        5   /* backward: delta = dO . W, then dQ over active tiles */
+#define EA_STAGE_DQ        5   /* backward: delta, then dQ, over active tiles */
 #define EA_STAGE_DKDV      6   /* backward: dK, dV over active tiles */
 #define EA_NUM_STAGES      7
 
@@ -104,11 +104,6 @@ typedef struct {
  * copies of V (forward) or of K, Q, dO (backward).  O(B*H*N*d + B*H*n_qt*n_kt); no
  * N^2-element buffer.  Returns 0 for an invalid desc. */
 size_t entmax_attn_workspace_bytes(const ea_desc* desc);
-
-/* Bytes of the forward -> backward carry `aux`: float32 [B, H, N, d] holding
- * w_i = sum_j u_ij v_j / sum_j u_ij, so that delta_i = dO_i . w_i.
- * Returns 0 for an invalid desc. */
-size_t entmax_attn_aux_bytes(const ea_desc* desc);
 
 /* Shape of block_mask: [B, H, n_qt, n_kt] bytes with n_qt = ceil(N/bm),
  * n_kt = ceil(N/bn).  Any output pointer may be NULL.  Returns a status. */
@@ -121,7 +116,6 @@ int entmax_attn_mask_dims(const ea_desc* desc, int* n_qt, int* n_kt, int* bm, in
  *  block_mask  uint8 [B,H,n_qt,n_kt] (mask_dims)      (written): 1 where the
  *              tile holds a visible entry with x > tau, 0 otherwise (a tile
  *              marked 1 may still be all-zero only within float32 rounding).
- *  aux         float32 [B,H,N,d] or NULL              (written if non-NULL; required by the backward)
  *  tau_iters   uint8 [B,H,N] or NULL                  (written if non-NULL):
  *              refinement sweeps that evaluated f(tau) for the row (the
  *              row-max and histogram sweeps are not counted).
@@ -129,16 +123,17 @@ int entmax_attn_mask_dims(const ea_desc* desc, int* n_qt, int* n_kt, int* bm, in
  *  ws          device workspace of ws_bytes >= entmax_attn_workspace_bytes(desc).
  */
 int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, int causal,
-                    void* out, float* tau, uint8_t* block_mask, void* aux, uint8_t* tau_iters,
+                    void* out, float* tau, uint8_t* block_mask, uint8_t* tau_iters,
                     const ea_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward pass.  tau, block_mask and aux must come from entmax_attn_fwd on the
- * same q, k, v, alpha, causal and desc.
+/* Backward pass.  tau and block_mask must come from entmax_attn_fwd on the
+ * same q, k, v, alpha, causal and desc (they are the only forward state the
+ * backward needs; delta_i = sum_j u_ij dP_ij / sum_j u_ij is recomputed).
  *  dout        [B,H,N,d] in_dtype                     (read)
  *  dq, dk, dv  [B,H,N,d] out_dtype                    (written)
  */
 int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, int causal,
-                    const void* dout, const float* tau, const uint8_t* block_mask, const void* aux,
+                    const void* dout, const float* tau, const uint8_t* block_mask,
                     void* dq, void* dk, void* dv,
                     const ea_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
