@@ -17,6 +17,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 VALU forms stay off on these parts
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the VALU epilogues read them without
+    # v_accvgpr_read copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -38,6 +38,7 @@
 #include <math.h>
 #include <float.h>
 
+#include <climits>
 #include <type_traits>
 
 #include "entmax_attn.h"
@@ -297,17 +298,27 @@ __device__ __forceinline__ void scores_T(f32x16 (&acc)[2], const char* klds, int
   }
 }
 
-// Mask invisible entries of an S^T tile (rows = keys key0.., column = query iq).
-__device__ __forceinline__ void mask_T(f32x16 (&acc)[2], int key0, int iq, int N, int causal,
-                                       int h) {
-  const bool qok = iq < N;
+// Visibility limit of this lane's query in an S^T tile whose rows are keys
+// key0..key0+63: rows r <= limit are visible (limit < 0: none).  Folding the
+// lane-half offset 4h of acc_row() in leaves one compare per element.
+__device__ __forceinline__ int row_limit(int key0, int iq, int N, int causal, int h) {
+  const int last = iq >= N ? -1 : (causal ? min(iq, N - 1) : N - 1) - key0;
+  return last - 4 * h;
+}
+__device__ __forceinline__ void mask_rows_above(f32x16 (&acc)[2], int lim) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int j = key0 + 32 * kb + acc_row(i, h);
-      if (!qok || j >= N || (causal && j > iq)) acc[kb][i] = -INFINITY;
-    }
+    for (int i = 0; i < 16; ++i)
+      if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) acc[kb][i] = -INFINITY;
+}
+// Tile of S^T (keys x this wave's 32 queries), masked only when `masked`.
+template <typename E, int D, bool M>
+__device__ __forceinline__ void tile_scores(f32x16 (&acc)[2], const char* kl, int ks,
+                                            const Frag<E> (&qf)[D / 16], int lane, int lim,
+                                            std::integral_constant<bool, M>) {
+  scores_T<E, D>(acc, kl, ks, qf, lane);
+  if constexpr (M) mask_rows_above(acc, lim);
 }
 
 template <typename E, int D>
@@ -491,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      if constexpr (decltype(masked)::value) mask_T(acc[qb], kt * kBK, iq[qb], N, P.causal, h);
+      if constexpr (decltype(masked)::value) mask_rows_above(acc[qb], row_limit(kt * kBK, iq[qb], N, P.causal, h));
       float tm = fmaxf(acc[qb][0][0], acc[qb][1][0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) tm = fmaxf(tm, fmaxf(acc[qb][0][i], acc[qb][1][i]));
@@ -528,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
 // Halley / bisection sweeps over candidate tiles, tau, iteration counts and
 // the block mask.  Dynamic LDS: K double buffer | histogram [128][BINS][2] u64 |
 // list i16[kChunk] | wave bits u8[kChunk] | flags u8[kChunk] | per-wave state.
-constexpr int kChunk = 1024;   // key tiles listed at once
+constexpr int kChunk = 512;    // key tiles listed at once
 
 template <typename E, int D, int AK, int BINS>
 __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
@@ -616,22 +627,27 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         const int kt = base + list[i];
         if (i + 1 < n) st.load(Kh, (base + list[i + 1]) * kBK, N);
         if ((wbits[i] >> w) & 1) {
-          f32x16 acc[2];
-          scores_T<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane);
-          const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
-          if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
+          auto body = [&](auto masked) {
+            f32x16 acc[2];
+            tile_scores<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane,
+                              row_limit(kt * kBK, iq, N, P.causal, h), masked);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const float y = fmaf(acc[kb][j], P.scale, -lo);
-              if (y > 0.0f) {
-                const unsigned Y = (unsigned)(y * 16777216.0f);
-                const int b = min((int)(Y >> SHIFT), BINS - 1);
-                atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
-                atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
+              for (int j = 0; j < 16; ++j) {
+                const float y = fmaf(acc[kb][j], P.scale, -lo);
+                if (y > 0.0f) {
+                  const unsigned Y = (unsigned)(y * 16777216.0f);
+                  const int b = min((int)(Y >> SHIFT), BINS - 1);
+                  atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
+                  atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
+                }
               }
-            }
+          };
+          if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+            body(std::true_type{});
+          else
+            body(std::false_type{});
         }
         if (i + 1 < n) st.store(kbuf + ((i + 1) & 1) * kBK * KS, KS);
         __syncthreads();
@@ -738,22 +754,27 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         const int kt = base + list[i];
         if (i + 1 < n) st.load(Kh, (base + list[i + 1]) * kBK, N);
         if (wave_busy && ((wbits[i] >> w) & 1)) {
-          f32x16 acc[2];
-          scores_T<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane);
-          const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
-          if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
-          const float before = Ent<AK>::count(F0, F1, F2, cnt);
+          auto body = [&](auto masked) {
+            f32x16 acc[2];
+            tile_scores<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane,
+                              row_limit(kt * kBK, iq, N, P.causal, h), masked);
+            const float before = Ent<AK>::count(F0, F1, F2, cnt);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
-              Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
+              for (int j = 0; j < 16; ++j) {
+                const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
+                Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
+              }
+            if (!dense) {
+              const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
+              if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
             }
-          if (!dense) {
-            const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
-            if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
-          }
+          };
+          if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+            body(std::true_type{});
+          else
+            body(std::false_type{});
         }
         if (i + 1 < n) st.store(kbuf + ((i + 1) & 1) * kBK * KS, KS);
         __syncthreads();
@@ -811,7 +832,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
 // block mask.  bf16: V tiles are staged as rows and read down their columns with
 // transposed LDS reads; fp32: Vsrc is a V^T copy [BH][D][Np].
 template <typename E, int D, int AK>
-__global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const E* __restrict__ K,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 4 && D == 128 ? 1 : 2, 2))) void k_pv(const E* __restrict__ Q, const E* __restrict__ K,
                                                  const E* __restrict__ Vsrc,
                                                  const float* __restrict__ tau_in,
                                                  const uint8_t* __restrict__ mask, Params P,
@@ -876,38 +897,42 @@ __global__ __launch_bounds__(kThreads) void k_pv(const E* __restrict__ Q, const 
       if ((wbits[i] >> w) & 1) {
         const char* kl = kbuf + (i & 1) * kBK * KS;
         const char* vl = vbuf + (i & 1) * VT;
-        f32x16 acc[2];
-        scores_T<E, D>(acc, kl, KS, qf, lane);
-        const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
-        if (need) mask_T(acc, kt * kBK, iq, N, P.causal, h);
+        auto body = [&](auto masked) {
+          f32x16 acc[2];
+          tile_scores<E, D>(acc, kl, KS, qf, lane, row_limit(kt * kBK, iq, N, P.causal, h), masked);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
-            float p, u;
-            Ent<AK>::pu(t, P.beta, p, u);
-            acc[kb][j] = p;
-          }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            Frag<E> pf;
-            from_acc(pf, acc[kb], 8 * s);
-            const int koff = 32 * kb + 16 * s + 4 * h;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-              Frag<E> vf;
-              if constexpr (kTr) {
-                ld_col8(vf, vl, VS, koff, 32 * db, lane);
-              } else {
-                const E* vrow = reinterpret_cast<const E*>(vl + (32 * db + c32) * VS);
-                ld4x2(vf, vrow + koff, vrow + koff + 8);
-              }
-              mma(oacc[db], vf, pf);
+            for (int j = 0; j < 16; ++j) {
+              const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
+              float p, u;
+              Ent<AK>::pu(t, P.beta, p, u);
+              acc[kb][j] = p;
             }
-          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+              Frag<E> pf;
+              from_acc(pf, acc[kb], 8 * s);
+              const int koff = 32 * kb + 16 * s + 4 * h;
+#pragma unroll
+              for (int db = 0; db < D / 32; ++db) {
+                Frag<E> vf;
+                if constexpr (kTr) {
+                  ld_col8(vf, vl, VS, koff, 32 * db, lane);
+                } else {
+                  const E* vrow = reinterpret_cast<const E*>(vl + (32 * db + c32) * VS);
+                  ld4x2(vf, vrow + koff, vrow + koff + 8);
+                }
+                mma(oacc[db], vf, pf);
+              }
+            }
+        };
+        if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+          body(std::true_type{});
+        else
+          body(std::false_type{});
       }
       if (i + 1 < n) store((i + 1) & 1);
       __syncthreads();
@@ -959,7 +984,7 @@ __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ in, E* 
 // where dP^T = V dO^T, all in the S^T layout.  bf16 reads the dQ operand
 // down the columns of the staged K tile; fp32 stages K^T too.
 template <typename E, int D, int AK, int NB>
-__global__ __launch_bounds__(kThreads) void k_bwd_dq(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 && D == 64 && AK == AK15 ? 2 : 1, 2))) void k_bwd_dq(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Kt, const float* __restrict__ tau_in,
     const uint8_t* __restrict__ mask, Params P, float* __restrict__ delta_out,
@@ -1034,56 +1059,60 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
         if ((wbits[i] >> w) & 1) {
           const int buf = NB == 2 ? (i & 1) : 0;
           const char* kl = kbuf + buf * kBK * KS;
-          f32x16 sacc[2], pacc[2];
-          scores_T<E, D>(sacc, kl, KS, qf, lane);
-          scores_T<E, D>(pacc, vbuf + buf * kBK * KS, KS, of, lane);
-          const bool need = wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0);
-          if (need) mask_T(sacc, kt * kBK, iq, N, P.causal, h);
-          if (pass == 0) {
+          auto body = [&](auto masked) {
+            f32x16 sacc[2], pacc[2];
+            tile_scores<E, D>(sacc, kl, KS, qf, lane, row_limit(kt * kBK, iq, N, P.causal, h), masked);
+            scores_T<E, D>(pacc, vbuf + buf * kBK * KS, KS, of, lane);
+            if (pass == 0) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+              for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int j = 0; j < 16; ++j) {
-                const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
-                float p, u;
-                Ent<AK>::pu(t, P.beta, p, u);
-                num = fmaf(u, pacc[kb][j], num);
-                den += u;
-              }
-          } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int j = 0; j < 16; ++j) {
-                const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
-                float p, u;
-                Ent<AK>::pu(t, P.beta, p, u);
-                sacc[kb][j] = u * (pacc[kb][j] - dlt);
-              }
-            const char* tl = tbuf + buf * TT;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int s = 0; s < 2; ++s) {
-                // dQ = sum_j dS_ij k_j cancels strongly when the supporting keys are
-                // nearly parallel (sum_j dS_ij = 0): dS goes in as a hi/lo bf16 pair.
-                Frag<E> sf, sl;
-                split_acc(sf, sl, sacc[kb], 8 * s);
-                const int koff = 32 * kb + 16 * s + 4 * h;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                  Frag<E> kf;
-                  if constexpr (kTr) {
-                    ld_col8(kf, kl, KS, koff, 32 * db, lane);
-                  } else {
-                    const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
-                    ld4x2(kf, krow + koff, krow + koff + 8);
-                  }
-                  mma(gacc[db], kf, sf);
-                  if constexpr (kNeedsLo<E>) mma(gacc[db], kf, sl);
+                for (int j = 0; j < 16; ++j) {
+                  const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
+                  float p, u;
+                  Ent<AK>::pu(t, P.beta, p, u);
+                  num = fmaf(u, pacc[kb][j], num);
+                  den += u;
                 }
-              }
-          }
+            } else {
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                  const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
+                  float p, u;
+                  Ent<AK>::pu(t, P.beta, p, u);
+                  sacc[kb][j] = u * (pacc[kb][j] - dlt);
+                }
+              const char* tl = tbuf + buf * TT;
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                  // dQ = sum_j dS_ij k_j cancels strongly when the supporting keys are
+                  // nearly parallel (sum_j dS_ij = 0): dS goes in as a hi/lo bf16 pair.
+                  Frag<E> sf, sl;
+                  split_acc(sf, sl, sacc[kb], 8 * s);
+                  const int koff = 32 * kb + 16 * s + 4 * h;
+#pragma unroll
+                  for (int db = 0; db < D / 32; ++db) {
+                    Frag<E> kf;
+                    if constexpr (kTr) {
+                      ld_col8(kf, kl, KS, koff, 32 * db, lane);
+                    } else {
+                      const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
+                      ld4x2(kf, krow + koff, krow + koff + 8);
+                    }
+                    mma(gacc[db], kf, sf);
+                    if constexpr (kNeedsLo<E>) mma(gacc[db], kf, sl);
+                  }
+                }
+            }
+          };
+          if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+            body(std::true_type{});
+          else
+            body(std::false_type{});
         }
         if (i + 1 < n) {
           if (NB == 1) __syncthreads();
@@ -1124,7 +1153,7 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dq(
 // the B operand runs down the columns of the staged Q / dO tiles (bf16:
 // transposed LDS reads; fp32: staged Q^T / dO^T copies).
 template <typename E, int D, int AK>
-__global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 && D == 64 ? 2 : 1, 2))) void k_bwd_dkdv(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Qt, const E* __restrict__ dOt,
     const float* __restrict__ tau_in, const float* __restrict__ delta_in,
@@ -1233,18 +1262,30 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dkdv(
           ld8(b, reinterpret_cast<const E*>(otl + c32 * KS) + 16 * c + 8 * h);
           mma(pacc, b, vf[c]);
         }
+        // query rows r (acc_row) are visible to this lane's key when
+        // jk - qb0 <= r <= N - 1 - qb0 (causal) and the key exists
+        auto softmax_like = [&](auto masked) {
+          const int rlo = (P.causal ? jk - qb0 : INT_MIN / 2) - 4 * h;
+          const int rhi = (kvalid ? N - 1 - qb0 : -1) - 4 * h;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int qr = acc_row(j, h);
-          const int qi = qb0 + qr;
-          float sv = sacc[j];
-          if (!kvalid || qi >= N || (P.causal && jk > qi)) sv = -INFINITY;
-          const float t = clamp01(fmaf(sv, P.scale, -taus[qr]));
-          float pp, u;
-          Ent<AK>::pu(t, P.beta, pp, u);
-          sacc[j] = pp;
-          pacc[j] = u * (pacc[j] - dels[qr]);
-        }
+          for (int j = 0; j < 16; ++j) {
+            const int qr = acc_row(j, h);
+            float sv = sacc[j];
+            if constexpr (decltype(masked)::value) {
+              const int r0 = 8 * (j >> 2) + (j & 3);
+              if (r0 < rlo || r0 > rhi) sv = -INFINITY;
+            }
+            const float t = clamp01(fmaf(sv, P.scale, -taus[qr]));
+            float pp, u;
+            Ent<AK>::pu(t, P.beta, pp, u);
+            sacc[j] = pp;
+            pacc[j] = u * (pacc[j] - dels[qr]);
+          }
+        };
+        if (qb0 + kBQ > N || (P.causal && kw0 + 31 > qb0) || kw0 + 32 > N)
+          softmax_like(std::true_type{});
+        else
+          softmax_like(std::false_type{});
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           Frag<E> pf, sf;

@@ -126,6 +126,11 @@ def main():
     ap.add_argument("--workload", default="planted_16k")
     ap.add_argument("--tau-mode", default="hist", choices=["hist", "halley", "bisect"])
     ap.add_argument("--cpu-heads", type=int, default=1, help="heads the CPU oracle is timed on (0 = skip)")
+    ap.add_argument("--strength", type=float, default=None,
+                    help="planted workloads: query strength a (Q = a*c + noise); sets the sparsity")
+    ap.add_argument("--alpha", type=float, default=None, help="override the workload's alpha")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 512 MiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -136,7 +141,12 @@ def main():
     import adaptive_sparse_flash_amd as A
     from gen import inputs as G
 
-    w = G.workload(args.workload)
+    over = {}
+    if args.strength is not None:
+        over["strength"] = args.strength
+    if args.alpha is not None:
+        over["alpha"] = args.alpha
+    w = G.workload(args.workload, **over)
     x = G.make_inputs(w)
     dt_in = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -147,6 +157,15 @@ def main():
     def step():
         bufs.forward(q, k, v, w.alpha, w.causal)
         bufs.backward(q, k, v, do, w.alpha, w.causal)
+
+    if args.copy_calibration:
+        # 512 MiB read + 512 MiB written by one elementwise copy kernel
+        src = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -203,7 +222,7 @@ def main():
         "config": {
             "workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
                         f"{'causal' if w.causal else 'non-causal'} alpha={w.alpha} {w.gen}"
-                        + (f" span={w.span}" if w.gen == "planted" else f" scale={w.scale}"),
+                        + (f" span={w.span} strength={w.strength}" if w.gen == "planted" else f" scale={w.scale}"),
             "tau_mode": args.tau_mode,
             "block_sparsity_32x64": sp32,
             "block_sparsity_128x64": sp128,
