@@ -54,6 +54,7 @@ constexpr int kThreads = kWave * kWaves;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
@@ -195,6 +196,22 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
   v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// OR over each 32-lane half of the wave: returns the half-0 result in the low
+// and the half-1 result in the high 32 bits (wave-uniform).
+__device__ __forceinline__ unsigned long long half_or_dpp(uint32_t v) {
+  v |= dpp_u<0xB1>(v);
+  v |= dpp_u<0x4E>(v);
+  v |= dpp_u<0x141>(v);
+  v |= dpp_u<0x140>(v);
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0) | (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 32) | (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return (unsigned long long)a | ((unsigned long long)b << 32);
 }
 
 // ------------------------------------------------------ entmax powers ---
@@ -441,16 +458,40 @@ __device__ __forceinline__ int build_list(int base, int len, Pred pred, short* l
   return *counter;
 }
 
+// Tile maxima are kept as IEEE half bits rounded toward +infinity: the stored
+// value bounds the true maximum from above and the half just below it bounds
+// it from below (strictly), which is all the pruning and the lower bracket
+// end need, at half the bytes of fp32.
+__device__ __forceinline__ uint16_t half_bits_up(float x) {
+  const _Float16 hx = (_Float16)x;
+  uint16_t b = __builtin_bit_cast(uint16_t, hx);
+  if ((float)hx < x) b = (b & 0x8000u) ? (uint16_t)(b - 1u) : (uint16_t)(b + 1u);
+  return b;
+}
+__device__ __forceinline__ float half_up_value(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+// the half just below the stored one (-inf stays -inf)
+__device__ __forceinline__ float half_down_value(uint16_t b) {
+  uint16_t d;
+  if (b == 0xFC00u) d = b;
+  else if (b == 0x0000u || b == 0x8000u) d = 0x8001u;
+  else d = (b & 0x8000u) ? (uint16_t)(b + 1u) : (uint16_t)(b - 1u);
+  return (float)__builtin_bit_cast(_Float16, d);
+}
+
 // ---------------------------------------------------------- k_rowmax ---
 // The one full score sweep: per-row maxima of x = (alpha-1) q.k / sqrt(d)
-// and, per (32 queries) x (64 keys) tile, the maximum raw score (used to
-// prune key tiles that can never hold a nonzero probability).  Each wave
+// and, for every row and 64-key tile, the row's maximum x over the tile
+// (tilemax[bh][row][kt], rows padded to a multiple of 8 tiles, as half bits
+// rounded up; it bounds tau from below and prunes key tiles that can never
+// hold a nonzero probability).  Each wave
 // owns 64 queries (two B-operand blocks share every K fragment read from
 // LDS); the workgroup (256 queries) streams K tiles double-buffered.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, const E* __restrict__ K,
                                                      Params P, float* __restrict__ rowmax,
-                                                     float* __restrict__ tilemax) {
+                                                     uint16_t* __restrict__ tilemax) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KS = row_stride<E, D>();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
@@ -484,8 +525,23 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   }
   __syncthreads();
 
+  const int ktp = (P.n_kt + 7) & ~7;   // tile maxima row length
+  // Each lane collects its row's last 8 tile maxima (a 16-byte shift register
+  // of halves, oldest lowest) and stores them together.
+  const int my_row = h ? iq[1] : iq[0];
+  u32x4 tbuf = u32x4{0xFC00FC00u, 0xFC00FC00u, 0xFC00FC00u, 0xFC00FC00u};
+  auto push = [&](uint32_t hb) {
+    tbuf[0] = __builtin_amdgcn_alignbit(tbuf[1], tbuf[0], 16);
+    tbuf[1] = __builtin_amdgcn_alignbit(tbuf[2], tbuf[1], 16);
+    tbuf[2] = __builtin_amdgcn_alignbit(tbuf[3], tbuf[2], 16);
+    tbuf[3] = __builtin_amdgcn_alignbit(hb, tbuf[3], 16);
+  };
+  auto flush = [&](int kt8) {
+    if (my_row < N) *reinterpret_cast<u32x4*>(tilemax + ((size_t)bh * N + my_row) * ktp + kt8) = tbuf;
+  };
   // one tile: scores for both query blocks, optional masking, maxima
   auto tile = [&](int kt, auto masked) {
+    float tmax[2];
     const char* kl = smem + (kt & 1) * kBK * KS;
     f32x16 acc[2][2];
 #pragma unroll
@@ -507,10 +563,14 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
 #pragma unroll
       for (int i = 1; i < 16; ++i) tm = fmaxf(tm, fmaxf(acc[qb][0][i], acc[qb][1][i]));
       m[qb] = fmaxf(m[qb], tm);
-      const float wm = wave_max_dpp(tm);
-      const int r32 = (wq0 >> 5) + qb;
-      if (lane == 0 && r32 < P.n_q32) tilemax[((size_t)bh * P.n_q32 + r32) * P.n_kt + kt] = wm;
+      tmax[qb] = tm;
     }
+    // each row's maximum over the tile (lanes l and l^32 hold its two
+    // halves); lane half h stores the value of query block h
+    const float r0 = fmaxf(tmax[0], __shfl_xor(tmax[0], 32));
+    const float r1 = fmaxf(tmax[1], __shfl_xor(tmax[1], 32));
+    push(half_bits_up((h ? r1 : r0) * P.scale));
+    if ((kt & 7) == 7) flush(kt & ~7);
   };
 
   int kt = 0;
@@ -526,6 +586,13 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
     if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
     __syncthreads();
   }
+  // the last, partial group of tile maxima (tiles up to the padded row end
+  // read as -inf)
+  const int n_done = max(kt_end_w, kt_full);
+  if (n_done & 7) {
+    for (int r = n_done & 7; r < 8; ++r) push(0xFC00u);
+    flush(n_done & ~7);
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float mm = fmaxf(m[qb], __shfl_xor(m[qb], 32));
@@ -534,17 +601,18 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
 }
 
 // ------------------------------------------------------------- k_tau ---
-// Per workgroup (128 queries, 32 per wave): bracket from the row maxima,
-// candidate key tiles from the tile maxima, histogram initialisation,
+// Per workgroup (128 queries, 32 per wave): bracket from the row maxima and
+// the row's tile maxima, candidate key tiles, histogram initialisation,
 // Halley / bisection sweeps over candidate tiles, tau, iteration counts and
-// the block mask.  Dynamic LDS: K double buffer | histogram [128][BINS][2] u64 |
-// list i16[kChunk] | wave bits u8[kChunk] | flags u8[kChunk] | per-wave state.
+// the block mask.  Dynamic LDS: K double buffer | histogram [128][BINS*2+2] u64 |
+// list i16[kChunk] | wave bits u8[kChunk] | flags u8[kChunk] |
+// candidate bits u32[4][n_words] | counter.
 constexpr int kChunk = 512;    // key tiles listed at once
 
 template <typename E, int D, int AK, int BINS>
 __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
                                                   const float* __restrict__ rowmax,
-                                                  const float* __restrict__ tilemax, Params P,
+                                                  const uint16_t* __restrict__ tilemax, Params P,
                                                   float* __restrict__ tau_out,
                                                   uint8_t* __restrict__ mask_out,
                                                   uint8_t* __restrict__ iters_out) {
@@ -564,21 +632,44 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   const E* Kh = K + (size_t)bh * N * D;
   const bool dense = (P.flags & EA_FLAG_FORCE_DENSE) != 0;
 
+  // histogram rows are padded by one bin so the 32 rows of a wave updating
+  // the same bin index do not hit the same LDS bank
+  constexpr int HROW = BINS * 2 + 2;
+  const int n_words = (P.n_kt + 31) >> 5;
   char* kbuf = smem;                                                  // 2 x [64][KS]
   unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem + 2 * kBK * KS);
-  short* list = reinterpret_cast<short*>(hist + kBQW * BINS * 2);
+  short* list = reinterpret_cast<short*>(hist + kBQW * HROW);
   uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
   uint8_t* flags = wbits + kChunk;
-  float* lo_wave = reinterpret_cast<float*>(flags + kChunk);          // [4]
-  int* kt_end_wave = reinterpret_cast<int*>(lo_wave + kWaves);        // [4]
-  int* counter = kt_end_wave + kWaves;
+  uint32_t* cbits = reinterpret_cast<uint32_t*>(flags + kChunk);      // [4][n_words]
+  int* counter = reinterpret_cast<int*>(cbits + kWaves * n_words);
 
-  Frag<E> qf[D / 16];
-  load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
   const int wq_last = min(N - 1, wq0 + kBQ - 1);
   const int kt_end_w = !wave_rows ? 0 : (P.causal ? wq_last / kBK + 1 : P.n_kt);
   const int kt_end = P.causal ? (min(N - 1, q0 + kBQW - 1) / kBK + 1) : P.n_kt;
   const bool wave_has_tail = wq0 + kBQ > N;
+
+  const int ktp = (P.n_kt + 7) & ~7;
+  // this row's tile maxima; lane half h reads the groups of 8 tiles 2i + h
+  const uint16_t* tmx = tilemax + ((size_t)bh * N + (valid ? iq : 0)) * ktp;
+  // 2 kGB groups of 8 tiles (kGB per lane half) per batch
+  constexpr int kGB = AK == AKGEN ? 4 : 8;
+  auto load_groups = [&](int g0, u32x4 (&r)[kGB]) {
+#pragma unroll
+    for (int u = 0; u < kGB; ++u) {
+      const int g = g0 + 2 * u + h;
+      if (valid && g * 8 < kt_end_w)
+        r[u] = *reinterpret_cast<const u32x4*>(tmx + g * 8);
+      else
+        r[u] = u32x4{0xFC00FC00u, 0xFC00FC00u, 0xFC00FC00u, 0xFC00FC00u};
+    }
+  };
+  // the first batch is in flight together with the query fragments
+  u32x4 pre[kGB];
+  load_groups(0, pre);
+
+  Frag<E> qf[D / 16];
+  load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
 
   // ---- provable bracket [lo, hi]:  f(max x - 1) >= 0 >= f(max x - n^(1-alpha))
   const float xmax = valid ? rowmax[(size_t)bh * N + iq] : 0.0f;
@@ -595,26 +686,123 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   }
   bool conv = !valid;
   int iters = 0;
-  const float lo_w = wave_min(valid ? lo : INFINITY);
-  if (lane == 0) {
-    lo_wave[w] = lo_w;
-    kt_end_wave[w] = kt_end_w;
-  }
-  __syncthreads();
-  // A key tile can hold a nonzero probability for wave ww only if its largest
-  // score reaches the wave's lowest lower bracket end (tau >= lo always).
-  const float* tmx = tilemax + ((size_t)bh * P.n_q32 + (size_t)qtile * kWaves) * P.n_kt;
-  auto cand = [&](int ww, int kt) -> bool {
-    if (kt >= kt_end_wave[ww]) return false;
-    if (dense) return true;
-    return tmx[(size_t)ww * P.n_kt + kt] * P.scale >= lo_wave[ww];
+  const double beta = (double)P.beta;
+  int* ncand = counter + 1;                                   // [4]
+  // half bits of tile g*8 + j from a loaded group (-inf past the wave's end)
+  auto group_half = [&](const u32x4& r, int g, int j) -> uint16_t {
+    const uint32_t wrd = r[j >> 1];
+    const uint16_t b = (uint16_t)((j & 1) ? (wrd >> 16) : (wrd & 0xFFFFu));
+    return (g * 8 + j < kt_end_w) ? b : (uint16_t)0xFC00u;
   };
+
+  // ---- candidate key tiles: bit kt of wave w is set when some row of the
+  // wave has a tile maximum above its lower bracket end (tau >= lo, so no
+  // other tile can hold a nonzero probability for the wave).  Returns the
+  // workgroup's number of candidate wave-tiles, counted as if skipping were
+  // on, so that every decision taken from it is the same either way.
+  auto make_cand = [&](auto use_pre) -> int {
+    __syncthreads();   // earlier readers of the bits and counts are done
+    const float lim = valid ? lo - 4.0f * FLT_EPSILON * fmaxf(1.0f, fabsf(lo)) : INFINITY;
+    int total = 0;
+    // batch of 16 kGB tiles = kGB / 2 words; group g = 2i + h covers tiles 8g..8g+7
+    for (int g0 = 0; g0 * 8 < kt_end; g0 += 2 * kGB) {   // later tiles are never listed
+      u32x4 r[kGB];
+      if (decltype(use_pre)::value && g0 == 0) {
+#pragma unroll
+        for (int u = 0; u < kGB; ++u) r[u] = pre[u];
+      } else {
+        load_groups(g0, r);
+      }
+      // this row's candidate bits, 8 per group, then OR over the half's rows
+      uint32_t pl[kGB / 4];
+#pragma unroll
+      for (int q = 0; q < kGB / 4; ++q) pl[q] = 0u;
+#pragma unroll
+      for (int u = 0; u < kGB; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (half_up_value(group_half(r[u], g0 + 2 * u + h, j)) > lim) pl[u >> 2] |= 1u << (8 * (u & 3) + j);
+#pragma unroll
+      for (int q = 0; q < kGB / 4; ++q) {
+        const unsigned long long hv = half_or_dpp(pl[q]);
+        const uint32_t h0 = (uint32_t)hv, h1 = (uint32_t)(hv >> 32);
+        // word k of this batch: groups g0+4k (half 0, u=2k), g0+4k+1 (half 1,
+        // u=2k), g0+4k+2 (half 0, u=2k+1), g0+4k+3 (half 1, u=2k+1)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int sh = 16 * kk;
+          const uint32_t real = ((h0 >> sh) & 0xFFu) | (((h1 >> sh) & 0xFFu) << 8) |
+                                (((h0 >> (sh + 8)) & 0xFFu) << 16) | (((h1 >> (sh + 8)) & 0xFFu) << 24);
+          const int wd = (g0 * 8 >> 5) + 2 * q + kk;
+          const int nv = min(max(kt_end_w - 32 * wd, 0), 32);
+          const uint32_t vis = nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+          total += __popc(real);
+          if (lane == 0 && wd < n_words) cbits[w * n_words + wd] = dense ? vis : real;
+        }
+      }
+    }
+    if (lane == 0) ncand[w] = total;
+    __syncthreads();
+    return ncand[0] + ncand[1] + ncand[2] + ncand[3];
+  };
+  auto cand = [&](int ww, int kt) -> bool { return (cbits[ww * n_words + (kt >> 5)] >> (kt & 31)) & 1u; };
+  // visible wave-tiles of the workgroup (the same for every thread)
+  int vis_total = 0;
+  for (int ww = 0; ww < kWaves; ++ww) {
+    const int wq = q0 + kBQ * ww;
+    if (wq < N) vis_total += P.causal ? min(N - 1, wq + kBQ - 1) / kBK + 1 : P.n_kt;
+  }
+  // Pruning pays for its extra passes over the tile maxima (a few memory
+  // round trips) only when the bracket [max x - 1, ...] leaves many tiles
+  // standing, both in number and as a share of the visible ones.
+  const int n_cand0 = make_cand(std::true_type{});
+  const bool wide = n_cand0 >= 64 && n_cand0 * 8 > vis_total;
+
+  // ---- lower bracket end from the row's tile maxima M_t.  Every tile holds
+  // its maximum element, so g(t) = sum_t [M_t - t]_+^beta - 1 <= f(t): g's root
+  // is a valid lower bound on tau, and a tight one when many tiles reach near
+  // the row maximum.  Halley-bisection on g over lower bounds of the tile
+  // maxima (the two lane halves take alternate tiles); the largest point with
+  // g >= 0 is kept.
+  if (wide && P.mode != EA_TAU_BISECT) {
+    float glo = lo, ghi = hi, tg = lo;
+    for (int it = 0; it < 3; ++it) {
+      float G0 = 0, G1 = 0, G2 = 0, gc = 0;
+      for (int g0 = 0; g0 * 8 < kt_end_w; g0 += 2 * kGB) {
+        u32x4 r[kGB];
+        load_groups(g0, r);
+#pragma unroll
+        for (int u = 0; u < kGB; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            Ent<AK>::sweep(clamp01(half_down_value(group_half(r[u], g0 + 2 * u + h, j)) - tg), P.beta,
+                           G0, G1, G2, gc);
+      }
+      G0 += __shfl_xor(G0, 32);
+      G1 += __shfl_xor(G1, 32);
+      G2 += __shfl_xor(G2, 32);
+      const double g = (double)G0 - 1.0;
+      if (g >= 0.0) glo = tg; else ghi = tg;
+      const double ulp = (double)FLT_EPSILON * fmax(1.0, fabs((double)tg));
+      const double gp = -beta * (double)G1;
+      const double gpp = (AK == AK20) ? 0.0 : beta * (beta - 1.0) * (double)G2;
+      const double th = (double)tg - 2.0 * g * gp / (2.0 * gp * gp - g * gpp);
+      float nt = (th > (double)glo && th < (double)ghi) ? (float)th : glo + 0.5f * (ghi - glo);
+      if (!(nt > glo && nt < ghi) || fabs(g) <= 2.0 * fabs(gp) * ulp || ghi - glo <= 4.0f * (float)ulp) break;
+      tg = nt;
+    }
+    glo -= 4.0f * FLT_EPSILON * fmaxf(1.0f, fabsf(glo));
+    if (valid && glo > lo) lo = fminf(glo, hi);
+    make_cand(std::false_type{});
+  }
 
   // ---- histogram initialisation (AdaSplash-2)
   if (P.mode == EA_TAU_HIST_HALLEY) {
-    for (int e = threadIdx.x; e < kBQW * BINS * 2; e += kThreads) hist[e] = 0ull;
-    constexpr int SHIFT = 24 - (BINS == 16 ? 4 : 3);
-    unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * BINS * 2;
+    for (int e = threadIdx.x; e < kBQW * HROW; e += kThreads) hist[e] = 0ull;
+    unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * HROW;
+    // bins split [lo, hi]; moments are kept in units of 2^-24 of y = x - lo <= 1
+    const float width = valid ? fmaxf(hi - lo, 1e-30f) : 1.0f;
+    const float bin_scale = (float)BINS / width;
     for (int base = 0; base < kt_end; base += kChunk) {
       const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
       RowStage<E, D, kBK> st;
@@ -637,8 +825,8 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
               for (int j = 0; j < 16; ++j) {
                 const float y = fmaf(acc[kb][j], P.scale, -lo);
                 if (y > 0.0f) {
-                  const unsigned Y = (unsigned)(y * 16777216.0f);
-                  const int b = min((int)(Y >> SHIFT), BINS - 1);
+                  const unsigned Y = (unsigned)(fminf(y, 1.0f) * 16777216.0f);
+                  const int b = min((int)(y * bin_scale), BINS - 1);
                   atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
                   atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
                 }
@@ -655,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     }
     if (valid) {
       const double inv24 = 1.0 / 16777216.0, inv48 = inv24 * inv24;
-      const double beta = (double)P.beta;
+      const double bw = (double)width / BINS;     // bin width in y = x - lo
       const bool exact = (AK == AK15 || AK == AK20);
       double C = 0, S1 = 0, S2 = 0;       // moments of the bins above the edge under test
       double f_hi = -1.0;                  // f at the upper edge of the bin under test
@@ -666,7 +854,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         const double cb = (double)(h1 >> 40);
         const double s1 = (double)(h1 & ((1ull << 40) - 1ull)) * inv24;
         const double s2 = (double)h2 * inv48;
-        const double e = (double)b / BINS;
+        const double e = (double)b * bw;
         const double Cn = C + cb, S1n = S1 + s1, S2n = S2 + s2;
         double f;
         if (AK == AK15) {
@@ -699,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         S1 = S1n;
         S2 = S2n;
       }
-      const double eb = (double)bstar / BINS, eb1 = (double)(bstar + 1) / BINS;
+      const double eb = (double)bstar * bw, eb1 = (double)(bstar + 1) * bw;
       double t0 = -1.0;
       if (exact && cstar == 0.0 && Cs > 0.0) {
         // the tau bin is empty: the support is exactly the bins above it
@@ -725,6 +913,8 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
       }
       tau = fminf(fmaxf(t0x, lo), hi);
     }
+    // the histogram narrowed lo to tau's bin: prune the candidates again
+    if (wide && (AK == AK15 || AK == AK20)) make_cand(std::false_type{});
   } else if (P.mode == EA_TAU_HALLEY_BISECT) {
     tau = lo;
   } else {
@@ -736,7 +926,6 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   if (wave_rows) {
     for (int kt = lane; kt < P.n_kt; kt += kWave) mrow[kt] = (dense && kt < kt_end_w) ? 1 : 0;
   }
-  const double beta = (double)P.beta;
   const int max_iters = P.max_iters;
   for (int sweep = 0; sweep <= max_iters + 1; ++sweep) {
     const bool wave_busy = __ballot(!conv) != 0ull;
@@ -1385,8 +1574,10 @@ size_t transposed_bytes(const Shape& s) {
   return s.esz == 4 ? align_up((size_t)s.BH * s.d * s.Np * s.esz, 256) : 0;
 }
 size_t row_bytes(const Shape& s) { return align_up((size_t)s.BH * s.N * sizeof(float), 256); }
+// one half per (row, 64-key tile), rows padded to a multiple of 8 tiles
 size_t tilemax_bytes(const Shape& s) {
-  return align_up((size_t)s.BH * s.n_q32 * s.n_kt * sizeof(float), 256);
+  const size_t ktp = (size_t)(s.n_kt + 7) / 8 * 8;
+  return align_up((size_t)s.BH * s.N * ktp * sizeof(uint16_t), 256);
 }
 
 size_t workspace_bytes(const Shape& s) {
@@ -1458,7 +1649,7 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   char* w = static_cast<char*>(ws);
   E* Vt = reinterpret_cast<E*>(w);
   float* rowmax = reinterpret_cast<float*>(w + transposed_bytes(s));
-  float* tilemax = reinterpret_cast<float*>(w + transposed_bytes(s) + row_bytes(s));
+  uint16_t* tilemax = reinterpret_cast<uint16_t*>(w + transposed_bytes(s) + row_bytes(s));
   int rc;
 
   tm.begin(EA_STAGE_FWD_PREP);
@@ -1475,7 +1666,8 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   tm.end(EA_STAGE_ROWMAX);
 
   constexpr int BINS = 16;
-  const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)kBQW * BINS * 16 + 4 * kChunk + 64;
+  const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)kBQW * (BINS * 2 + 2) * 8 + 4 * kChunk +
+                         (size_t)kWaves * ((s.n_kt + 31) / 32) * 4 + 64;
   auto ktau = k_tau<E, D, AK, BINS>;
   if ((rc = set_lds(ktau, tau_lds)) != EA_OK) return rc;
   const dim3 g(s.n_qt128 * s.BH);
