@@ -462,6 +462,10 @@ __device__ __forceinline__ int build_list(int base, int len, Pred pred, short* l
 // value bounds the true maximum from above and the half just below it bounds
 // it from below (strictly), which is all the pruning and the lower bracket
 // end need, at half the bytes of fp32.
+// Row length of the tile maxima: whole 64-byte segments (32 tiles), written
+// by one lane at once so that no partial segment reaches memory.
+__host__ __device__ constexpr int tilemax_row(int n_kt) { return (n_kt + 31) & ~31; }
+
 __device__ __forceinline__ uint16_t half_bits_up(float x) {
   const _Float16 hx = (_Float16)x;
   uint16_t b = __builtin_bit_cast(uint16_t, hx);
@@ -483,7 +487,7 @@ __device__ __forceinline__ float half_down_value(uint16_t b) {
 // ---------------------------------------------------------- k_rowmax ---
 // The one full score sweep: per-row maxima of x = (alpha-1) q.k / sqrt(d)
 // and, for every row and 64-key tile, the row's maximum x over the tile
-// (tilemax[bh][row][kt], rows padded to a multiple of 8 tiles, as half bits
+// (tilemax[bh][row][kt], rows padded to a multiple of 32 tiles, as half bits
 // rounded up; it bounds tau from below and prunes key tiles that can never
 // hold a nonzero probability).  Each wave
 // owns 64 queries (two B-operand blocks share every K fragment read from
@@ -525,19 +529,35 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   }
   __syncthreads();
 
-  const int ktp = (P.n_kt + 7) & ~7;   // tile maxima row length
-  // Each lane collects its row's last 8 tile maxima (a 16-byte shift register
-  // of halves, oldest lowest) and stores them together.
+  const int ktp = tilemax_row(P.n_kt);
+  // Each lane collects its row's tile maxima: the last 8 in a 16-byte shift
+  // register of halves (oldest lowest), groups of 8 in a kSeg-deep queue, and
+  // stores 8 kSeg tiles at once (64 bytes for d = 128; d = 64 keeps 16-byte
+  // stores, which spares the registers of a third wave per SIMD).
+  constexpr int kSeg = D == 64 ? 1 : 4;
   const int my_row = h ? iq[1] : iq[0];
-  u32x4 tbuf = u32x4{0xFC00FC00u, 0xFC00FC00u, 0xFC00FC00u, 0xFC00FC00u};
+  constexpr uint32_t kNegInf2 = 0xFC00FC00u;
+  u32x4 tbuf = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+  u32x4 gq[kSeg];
+#pragma unroll
+  for (int i = 0; i < kSeg; ++i) gq[i] = tbuf;
   auto push = [&](uint32_t hb) {
     tbuf[0] = __builtin_amdgcn_alignbit(tbuf[1], tbuf[0], 16);
     tbuf[1] = __builtin_amdgcn_alignbit(tbuf[2], tbuf[1], 16);
     tbuf[2] = __builtin_amdgcn_alignbit(tbuf[3], tbuf[2], 16);
     tbuf[3] = __builtin_amdgcn_alignbit(hb, tbuf[3], 16);
   };
-  auto flush = [&](int kt8) {
-    if (my_row < N) *reinterpret_cast<u32x4*>(tilemax + ((size_t)bh * N + my_row) * ktp + kt8) = tbuf;
+  auto push_group = [&]() {
+#pragma unroll
+    for (int i = 0; i + 1 < kSeg; ++i) gq[i] = gq[i + 1];
+    gq[kSeg - 1] = tbuf;
+  };
+  auto flush = [&](int kt0) {
+    if (my_row < N) {
+      u32x4* dst = reinterpret_cast<u32x4*>(tilemax + ((size_t)bh * N + my_row) * ktp + kt0);
+#pragma unroll
+      for (int i = 0; i < kSeg; ++i) dst[i] = gq[i];
+    }
   };
   // one tile: scores for both query blocks, optional masking, maxima
   auto tile = [&](int kt, auto masked) {
@@ -570,7 +590,10 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
     const float r0 = fmaxf(tmax[0], __shfl_xor(tmax[0], 32));
     const float r1 = fmaxf(tmax[1], __shfl_xor(tmax[1], 32));
     push(half_bits_up((h ? r1 : r0) * P.scale));
-    if ((kt & 7) == 7) flush(kt & ~7);
+    if ((kt & 7) == 7) {
+      push_group();
+      if (((kt >> 3) % kSeg) == kSeg - 1) flush(kt + 1 - 8 * kSeg);
+    }
   };
 
   int kt = 0;
@@ -586,12 +609,20 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
     if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
     __syncthreads();
   }
-  // the last, partial group of tile maxima (tiles up to the padded row end
+  // the last, partial segment of tile maxima (tiles up to the padded row end
   // read as -inf)
   const int n_done = max(kt_end_w, kt_full);
-  if (n_done & 7) {
-    for (int r = n_done & 7; r < 8; ++r) push(0xFC00u);
-    flush(n_done & ~7);
+  if (n_done % (8 * kSeg)) {
+    if (n_done & 7) {
+      for (int r = n_done & 7; r < 8; ++r) push(0xFC00u);
+      push_group();
+    }
+    const int filled = ((n_done + 7) >> 3) % kSeg;   // groups queued in the segment
+    if (filled) {
+      tbuf = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+      for (int g = filled; g < kSeg; ++g) push_group();
+    }
+    flush(n_done / (8 * kSeg) * (8 * kSeg));
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -649,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   const int kt_end = P.causal ? (min(N - 1, q0 + kBQW - 1) / kBK + 1) : P.n_kt;
   const bool wave_has_tail = wq0 + kBQ > N;
 
-  const int ktp = (P.n_kt + 7) & ~7;
+  const int ktp = tilemax_row(P.n_kt);
   // this row's tile maxima; lane half h reads the groups of 8 tiles 2i + h
   const uint16_t* tmx = tilemax + ((size_t)bh * N + (valid ? iq : 0)) * ktp;
   // 2 kGB groups of 8 tiles (kGB per lane half) per batch
@@ -1574,9 +1605,9 @@ size_t transposed_bytes(const Shape& s) {
   return s.esz == 4 ? align_up((size_t)s.BH * s.d * s.Np * s.esz, 256) : 0;
 }
 size_t row_bytes(const Shape& s) { return align_up((size_t)s.BH * s.N * sizeof(float), 256); }
-// one half per (row, 64-key tile), rows padded to a multiple of 8 tiles
+// one half per (row, 64-key tile), rows padded to a multiple of 32 tiles
 size_t tilemax_bytes(const Shape& s) {
-  const size_t ktp = (size_t)(s.n_kt + 7) / 8 * 8;
+  const size_t ktp = (size_t)tilemax_row(s.n_kt);
   return align_up((size_t)s.BH * s.N * ktp * sizeof(uint16_t), 256);
 }
 
