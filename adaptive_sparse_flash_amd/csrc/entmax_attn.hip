@@ -198,6 +198,12 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// max(x[l], x[l ^ 32]) on every lane, by one v_permlane32_swap
+__device__ __forceinline__ float half_swap_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
@@ -397,6 +403,53 @@ struct RowStage {
     }
   }
 };
+// Direct global -> LDS staging of a 64-row bf16 tile (buffer_load_dwordx4
+// ... lds: lane l of one instruction lands at LDS base + 16 l, no registers
+// involved).  Rows are stored unpadded; the 16-byte chunk c of row r sits in
+// slot c ^ (r mod chunks-per-row), so the 16 lanes of one ds_read_b128 phase
+// that read the same chunk of 16 consecutive rows hit 16 different bank
+// groups.  The buffer descriptor spans one head's N rows: rows past N read as
+// zeros (the hardware range check), and every reader masks them.
+template <int D>
+struct DirectTile {
+  static constexpr int RB = D * 2;                 // row bytes
+  static constexpr int CPR = RB / 16;              // chunks per row
+  static constexpr int BYTES = kBK * RB;
+  static constexpr int NI = BYTES / 1024 / kWaves; // instructions per wave
+  __amdgpu_buffer_rsrc_t rsrc;
+  int voff[NI];                                    // this lane's byte offsets in a tile
+  __device__ __forceinline__ DirectTile(const __bf16* head, int N, int w, int lane) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(head), (short)0, N * RB, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int p = (w * NI + i) * 1024 + 16 * lane;
+      const int r = p / RB, slot = (p % RB) / 16;
+      voff[i] = r * RB + ((slot ^ (r & (CPR - 1))) << 4);
+    }
+  }
+  // load key/value rows row0 .. row0+63 into `tile`
+  __device__ __forceinline__ void issue(char* tile, int row0, int w) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc,
+          reinterpret_cast<__attribute__((address_space(3))) void*>(
+              reinterpret_cast<uintptr_t>(tile + (w * NI + i) * 1024)),
+          16, voff[i], row0 * RB, 0, 0);
+  }
+  // address of chunk c (8 elements) of row r
+  __device__ __forceinline__ static const __bf16* at(const char* tile, int r, int c) {
+    return reinterpret_cast<const __bf16*>(tile + r * RB + ((c ^ (r & (CPR - 1))) << 4));
+  }
+};
+// Wait until at most n vector memory operations of this wave are in flight
+// (expcnt and lgkmcnt left at their maxima).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Columns col0..col0+W of a transposed [D][Np] matrix (all in range).
 template <typename E, int D, int W, int NT = kThreads>
 struct ColStage {
@@ -491,7 +544,9 @@ __device__ __forceinline__ float half_down_value(uint16_t b) {
 // rounded up; it bounds tau from below and prunes key tiles that can never
 // hold a nonzero probability).  Each wave
 // owns 64 queries (two B-operand blocks share every K fragment read from
-// LDS); the workgroup (256 queries) streams K tiles double-buffered.
+// LDS); the workgroup (256 queries) streams K tiles through LDS (bf16: three
+// stages filled by direct global->LDS loads; fp32: double-buffered through
+// registers).
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, const E* __restrict__ K,
                                                      Params P, float* __restrict__ rowmax,
@@ -522,12 +577,22 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
 
   float m[2] = {-INFINITY, -INFINITY};
+  constexpr bool kDirect = sizeof(E) == 2;
+  using DT = DirectTile<D>;
+  constexpr int NS = 3;                          // LDS stages of the direct pipeline
   RowStage<E, D, kBK> st;
-  if (kt_end > 0) {
-    st.load(Kh, 0, N);
-    st.store(smem, KS);
+  const DT dt(reinterpret_cast<const __bf16*>(Kh), N, w, lane);
+  if constexpr (kDirect) {
+    // tiles 0 and 1 in flight; each step waits for its own tile only
+    if (0 < kt_end) dt.issue(smem, 0, w);
+    if (1 < kt_end) dt.issue(smem + DT::BYTES, kBK, w);
+  } else {
+    if (kt_end > 0) {
+      st.load(Kh, 0, N);
+      st.store(smem, KS);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   const int ktp = tilemax_row(P.n_kt);
   // Each lane collects its row's tile maxima: the last 8 in a 16-byte shift
@@ -560,9 +625,10 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
     }
   };
   // one tile: scores for both query blocks, optional masking, maxima
+  int drain = 0;   // steps that wait for every memory operation (after stores)
   auto tile = [&](int kt, auto masked) {
     float tmax[2];
-    const char* kl = smem + (kt & 1) * kBK * KS;
+    const char* kl = kDirect ? smem + (kt % NS) * DT::BYTES : smem + (kt & 1) * kBK * KS;
     f32x16 acc[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
@@ -571,7 +637,10 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         Frag<E> a;
-        ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
+        if constexpr (kDirect)
+          ld8(a, DT::at(kl, 32 * kb + c32, 2 * c + h));
+        else
+          ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
         mma(acc[0][kb], a, qf[0][c]);
         mma(acc[1][kb], a, qf[1][c]);
       }
@@ -579,35 +648,61 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       if constexpr (decltype(masked)::value) mask_rows_above(acc[qb], row_limit(kt * kBK, iq[qb], N, P.causal, h));
-      float tm = fmaxf(acc[qb][0][0], acc[qb][1][0]);
+      // NaN-propagating maximum: v_maximum3_f32 with no canonicalising of the
+      // MFMA results that fmaxf would need
+      float tm = __builtin_elementwise_maximum(acc[qb][0][0], acc[qb][1][0]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) tm = fmaxf(tm, fmaxf(acc[qb][0][i], acc[qb][1][i]));
+      for (int i = 1; i < 16; ++i)
+        tm = __builtin_elementwise_maximum(tm, __builtin_elementwise_maximum(acc[qb][0][i], acc[qb][1][i]));
       m[qb] = fmaxf(m[qb], tm);
       tmax[qb] = tm;
     }
     // each row's maximum over the tile (lanes l and l^32 hold its two
     // halves); lane half h stores the value of query block h
-    const float r0 = fmaxf(tmax[0], __shfl_xor(tmax[0], 32));
-    const float r1 = fmaxf(tmax[1], __shfl_xor(tmax[1], 32));
+    const float r0 = half_swap_max(tmax[0]);
+    const float r1 = half_swap_max(tmax[1]);
     push(half_bits_up((h ? r1 : r0) * P.scale));
     if ((kt & 7) == 7) {
       push_group();
-      if (((kt >> 3) % kSeg) == kSeg - 1) flush(kt + 1 - 8 * kSeg);
+      if (((kt >> 3) % kSeg) == kSeg - 1) {
+        flush(kt + 1 - 8 * kSeg);
+        drain = NS - 1;
+      }
     }
   };
 
   int kt = 0;
-  for (; kt < kt_full; ++kt) {
-    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
-    tile(kt, std::false_type{});
-    if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
-    __syncthreads();
-  }
-  for (; kt < kt_end; ++kt) {
-    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
-    if (kt < kt_end_w) tile(kt, std::true_type{});
-    if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
-    __syncthreads();
+  if constexpr (kDirect) {
+    // Step kt: wait for tile kt (tile kt+1 may stay in flight unless stores
+    // were issued since), barrier, refill the stage freed by tile kt-1 with
+    // tile kt+2, compute tile kt.  Bare s_barrier: a full __syncthreads would
+    // wait for every load in flight.
+    auto step = [&](int kt, auto masked, bool compute) {
+      if (drain > 0 || kt + 1 >= kt_end) {
+        wait_vmcnt<0>();
+      } else {
+        wait_vmcnt<DT::NI>();
+      }
+      if (drain > 0) --drain;
+      __builtin_amdgcn_s_barrier();
+      if (kt + 2 < kt_end) dt.issue(smem + ((kt + 2) % NS) * DT::BYTES, (kt + 2) * kBK, w);
+      if (compute) tile(kt, masked);
+    };
+    for (; kt < kt_full; ++kt) step(kt, std::false_type{}, true);
+    for (; kt < kt_end; ++kt) step(kt, std::true_type{}, kt < kt_end_w);
+  } else {
+    for (; kt < kt_full; ++kt) {
+      if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
+      tile(kt, std::false_type{});
+      if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
+      __syncthreads();
+    }
+    for (; kt < kt_end; ++kt) {
+      if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
+      if (kt < kt_end_w) tile(kt, std::true_type{});
+      if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
+      __syncthreads();
+    }
   }
   // the last, partial segment of tile maxima (tiles up to the padded row end
   // read as -inf)
@@ -1689,7 +1784,7 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   tm.end(EA_STAGE_FWD_PREP);
 
   constexpr int KS = row_stride<E, D>();
-  const size_t rm_lds = (size_t)2 * kBK * KS;
+  const size_t rm_lds = sizeof(E) == 2 ? (size_t)3 * DirectTile<D>::BYTES : (size_t)2 * kBK * KS;
   auto krm = k_rowmax<E, D>;
   if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_ROWMAX);
