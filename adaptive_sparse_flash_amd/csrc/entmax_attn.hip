@@ -537,6 +537,63 @@ __device__ __forceinline__ float half_down_value(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, d);
 }
 
+// Each lane collects one row's tile maxima as half bits: the last 8 in a
+// 16-byte shift register (oldest lowest), groups of 8 in a SEG-deep queue, and
+// stores 8 SEG tiles (16 SEG bytes) at once at the row's position in
+// tilemax[bh][row][kt].  Nothing is stored for rows past N (row_ptr null).
+template <int SEG>
+struct TileMaxQueue {
+  static constexpr uint32_t kNegInf2 = 0xFC00FC00u;   // two half -inf
+  u32x4 tbuf;
+  u32x4 gq[SEG];
+  uint16_t* row_ptr;
+  __device__ __forceinline__ explicit TileMaxQueue(uint16_t* p) : row_ptr(p) {
+    tbuf = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) gq[i] = tbuf;
+  }
+  __device__ __forceinline__ void push(uint32_t hb) {
+    tbuf[0] = __builtin_amdgcn_alignbit(tbuf[1], tbuf[0], 16);
+    tbuf[1] = __builtin_amdgcn_alignbit(tbuf[2], tbuf[1], 16);
+    tbuf[2] = __builtin_amdgcn_alignbit(tbuf[3], tbuf[2], 16);
+    tbuf[3] = __builtin_amdgcn_alignbit(hb, tbuf[3], 16);
+  }
+  __device__ __forceinline__ void push_group() {
+#pragma unroll
+    for (int i = 0; i + 1 < SEG; ++i) gq[i] = gq[i + 1];
+    gq[SEG - 1] = tbuf;
+  }
+  __device__ __forceinline__ void flush(int kt0) {
+    if (row_ptr) {
+      u32x4* dst = reinterpret_cast<u32x4*>(row_ptr + kt0);
+#pragma unroll
+      for (int i = 0; i < SEG; ++i) dst[i] = gq[i];
+    }
+  }
+  // after tile kt's value was pushed; returns true when it stored a segment
+  __device__ __forceinline__ bool tile_done(int kt) {
+    if ((kt & 7) != 7) return false;
+    push_group();
+    if (((kt >> 3) % SEG) != SEG - 1) return false;
+    flush(kt + 1 - 8 * SEG);
+    return true;
+  }
+  // the last, partial segment after n_done tiles (the rest of it reads -inf)
+  __device__ __forceinline__ void finish(int n_done) {
+    if (n_done % (8 * SEG) == 0) return;
+    if (n_done & 7) {
+      for (int r = n_done & 7; r < 8; ++r) push(0xFC00u);
+      push_group();
+    }
+    const int filled = ((n_done + 7) >> 3) % SEG;   // groups queued in the segment
+    if (filled) {
+      tbuf = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
+      for (int g = filled; g < SEG; ++g) push_group();
+    }
+    flush(n_done / (8 * SEG) * (8 * SEG));
+  }
+};
+
 // ---------------------------------------------------------- k_rowmax ---
 // The one full score sweep: per-row maxima of x = (alpha-1) q.k / sqrt(d)
 // and, for every row and 64-key tile, the row's maximum x over the tile
@@ -595,35 +652,11 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   }
 
   const int ktp = tilemax_row(P.n_kt);
-  // Each lane collects its row's tile maxima: the last 8 in a 16-byte shift
-  // register of halves (oldest lowest), groups of 8 in a kSeg-deep queue, and
-  // stores 8 kSeg tiles at once (64 bytes for d = 128; d = 64 keeps 16-byte
-  // stores, which spares the registers of a third wave per SIMD).
+  // d = 128 stores 64-byte segments; d = 64 keeps 16-byte stores, which spares
+  // the registers of a third wave per SIMD
   constexpr int kSeg = D == 64 ? 1 : 4;
   const int my_row = h ? iq[1] : iq[0];
-  constexpr uint32_t kNegInf2 = 0xFC00FC00u;
-  u32x4 tbuf = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
-  u32x4 gq[kSeg];
-#pragma unroll
-  for (int i = 0; i < kSeg; ++i) gq[i] = tbuf;
-  auto push = [&](uint32_t hb) {
-    tbuf[0] = __builtin_amdgcn_alignbit(tbuf[1], tbuf[0], 16);
-    tbuf[1] = __builtin_amdgcn_alignbit(tbuf[2], tbuf[1], 16);
-    tbuf[2] = __builtin_amdgcn_alignbit(tbuf[3], tbuf[2], 16);
-    tbuf[3] = __builtin_amdgcn_alignbit(hb, tbuf[3], 16);
-  };
-  auto push_group = [&]() {
-#pragma unroll
-    for (int i = 0; i + 1 < kSeg; ++i) gq[i] = gq[i + 1];
-    gq[kSeg - 1] = tbuf;
-  };
-  auto flush = [&](int kt0) {
-    if (my_row < N) {
-      u32x4* dst = reinterpret_cast<u32x4*>(tilemax + ((size_t)bh * N + my_row) * ktp + kt0);
-#pragma unroll
-      for (int i = 0; i < kSeg; ++i) dst[i] = gq[i];
-    }
-  };
+  TileMaxQueue<kSeg> tq(my_row < N ? tilemax + ((size_t)bh * N + my_row) * ktp : nullptr);
   // one tile: scores for both query blocks, optional masking, maxima
   int drain = 0;   // steps that wait for every memory operation (after stores)
   auto tile = [&](int kt, auto masked) {
@@ -661,14 +694,8 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
     // halves); lane half h stores the value of query block h
     const float r0 = half_swap_max(tmax[0]);
     const float r1 = half_swap_max(tmax[1]);
-    push(half_bits_up((h ? r1 : r0) * P.scale));
-    if ((kt & 7) == 7) {
-      push_group();
-      if (((kt >> 3) % kSeg) == kSeg - 1) {
-        flush(kt + 1 - 8 * kSeg);
-        drain = NS - 1;
-      }
-    }
+    tq.push(half_bits_up((h ? r1 : r0) * P.scale));
+    if (tq.tile_done(kt)) drain = NS - 1;
   };
 
   int kt = 0;
@@ -704,26 +731,139 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
       __syncthreads();
     }
   }
-  // the last, partial segment of tile maxima (tiles up to the padded row end
-  // read as -inf)
-  const int n_done = max(kt_end_w, kt_full);
-  if (n_done % (8 * kSeg)) {
-    if (n_done & 7) {
-      for (int r = n_done & 7; r < 8; ++r) push(0xFC00u);
-      push_group();
-    }
-    const int filled = ((n_done + 7) >> 3) % kSeg;   // groups queued in the segment
-    if (filled) {
-      tbuf = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
-      for (int g = filled; g < kSeg; ++g) push_group();
-    }
-    flush(n_done / (8 * kSeg) * (8 * kSeg));
-  }
+  tq.finish(max(kt_end_w, kt_full));
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float mm = fmaxf(m[qb], __shfl_xor(m[qb], 32));
     if (iq[qb] < N && h == 0) rowmax[(size_t)bh * N + iq[qb]] = mm * P.scale;
   }
+}
+
+// The same sweep for bf16 inputs on 16x16x32 MFMA: sixteen independent
+// accumulators per wave (4 key blocks x 4 query blocks of 16) keep the matrix
+// pipe fed without dependent-issue stalls.  Operand layout of
+// v_mfma_f32_16x16x32_bf16 (lane l, g = l / 16): A[l % 16][8g + j],
+// B[8g + j][l % 16], C[4g + i][l % 16].  A = K rows, B = Q^T, so C is S^T and
+// lane l holds, for query (l % 16) of each query block, keys 4g + i of each
+// key block.
+__device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict__ Q,
+                                                       const __bf16* __restrict__ K, Params P,
+                                                       float* __restrict__ rowmax,
+                                                       uint16_t* __restrict__ tilemax) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  using DT = DirectTile<D>;
+  constexpr int NS = 3;            // LDS stages
+  constexpr int KST = D / 32;      // contraction steps of 32
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int N = P.N;
+  const int n_qt = (N + 255) / 256;
+  int bh, qtile;
+  map_tile(n_qt, P.BH, P.causal, bh, qtile);
+  const int q0 = qtile * 256;
+  const int wq0 = q0 + 64 * w;
+  const __bf16* Qh = Q + (size_t)bh * N * D;
+  const __bf16* Kh = K + (size_t)bh * N * D;
+
+  // B fragments: query wq0 + 16 b + c16, dimensions 32 ks + 8 g ... + 7
+  bf16x8 qf[4][KST];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int qi = wq0 + 16 * b + c16;
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks)
+      qf[b][ks] = qi < N ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qi * D + 32 * ks + 8 * g)
+                         : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  const int iq = wq0 + lane;       // the query whose maxima this lane keeps
+  const int kt_end = P.causal ? (min(N - 1, q0 + 255) / kBK + 1) : P.n_kt;
+  const int kt_end_w = wq0 >= N ? 0 : (P.causal ? (min(N - 1, wq0 + 63) / kBK + 1) : P.n_kt);
+  const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
+
+  const DT dt(Kh, N, w, lane);
+  if (0 < kt_end) dt.issue(smem, 0, w);
+  if (1 < kt_end) dt.issue(smem + DT::BYTES, kBK, w);
+
+  const int ktp = tilemax_row(P.n_kt);
+  constexpr int kSeg = D == 64 ? 1 : 4;
+  TileMaxQueue<kSeg> tq(iq < N ? tilemax + ((size_t)bh * N + iq) * ktp : nullptr);
+  float m = -INFINITY;
+  int drain = 0;
+
+  auto tile = [&](int kt, auto masked) {
+    const char* kl = smem + (kt % NS) * DT::BYTES;
+    f32x4 acc[4][4];               // [query block][key block]
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) acc[b][kb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KST; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(DT::at(kl, 16 * kb + c16, 4 * ks + g));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[b][kb] = mma16(a, qf[b][ks], acc[b][kb]);
+      }
+    if constexpr (decltype(masked)::value) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int qi = wq0 + 16 * b + c16;
+        // last visible key of query qi, relative to this lane's first key
+        const int lim = (qi >= N ? -1 : (P.causal ? min(qi, N - 1) : N - 1)) - kt * kBK - 4 * g;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * kb + i > lim) acc[b][kb][i] = -INFINITY;
+      }
+    }
+    float pm[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      float t = __builtin_elementwise_maximum(acc[b][0][0], acc[b][0][1]);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = (kb == 0 ? 2 : 0); i < 4; ++i) t = __builtin_elementwise_maximum(t, acc[b][kb][i]);
+      pm[b] = t;
+    }
+    // Reduce over the four lane groups and scatter: group g keeps query
+    // block g.  permlane32 swap pairs groups (0,2) and (1,3) for blocks
+    // (0,2) and (1,3); permlane16 swap then pairs (0,1) and (2,3).
+    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[0]), __float_as_uint(pm[2]), false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[1]), __float_as_uint(pm[3]), false, false);
+    const float a0 = __builtin_elementwise_maximum(__uint_as_float(s02[0]), __uint_as_float(s02[1]));
+    const float a1 = __builtin_elementwise_maximum(__uint_as_float(s13[0]), __uint_as_float(s13[1]));
+    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+    const float tm = __builtin_elementwise_maximum(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
+    m = fmaxf(m, tm);
+    tq.push(half_bits_up(tm * P.scale));
+    if (tq.tile_done(kt)) drain = NS - 1;
+  };
+
+  // Step kt: wait for tile kt (tile kt+1 may stay in flight unless stores
+  // were issued since), bare barrier, refill the stage freed by tile kt-1
+  // with tile kt+2, compute tile kt.
+  auto step = [&](int kt, auto masked, bool compute) {
+    if (drain > 0 || kt + 1 >= kt_end) {
+      wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<DT::NI>();
+    }
+    if (drain > 0) --drain;
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < kt_end) dt.issue(smem + ((kt + 2) % NS) * DT::BYTES, (kt + 2) * kBK, w);
+    if (compute) tile(kt, masked);
+  };
+  int kt = 0;
+  for (; kt < kt_full; ++kt) step(kt, std::false_type{}, true);
+  for (; kt < kt_end; ++kt) step(kt, std::true_type{}, kt < kt_end_w);
+  tq.finish(max(kt_end_w, kt_full));
+  if (iq < N) rowmax[(size_t)bh * N + iq] = m * P.scale;
 }
 
 // ------------------------------------------------------------- k_tau ---
@@ -1784,12 +1924,21 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   tm.end(EA_STAGE_FWD_PREP);
 
   constexpr int KS = row_stride<E, D>();
-  const size_t rm_lds = sizeof(E) == 2 ? (size_t)3 * DirectTile<D>::BYTES : (size_t)2 * kBK * KS;
-  auto krm = k_rowmax<E, D>;
-  if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
-  tm.begin(EA_STAGE_ROWMAX);
-  hipLaunchKernelGGL(krm, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, tilemax);
-  tm.end(EA_STAGE_ROWMAX);
+  if constexpr (sizeof(E) == 2) {
+    const size_t rm_lds = (size_t)3 * DirectTile<D>::BYTES;
+    auto krm = k_rowmax16<D>;
+    if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
+    tm.begin(EA_STAGE_ROWMAX);
+    hipLaunchKernelGGL(krm, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, tilemax);
+    tm.end(EA_STAGE_ROWMAX);
+  } else {
+    const size_t rm_lds = (size_t)2 * kBK * KS;
+    auto krm = k_rowmax<E, D>;
+    if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
+    tm.begin(EA_STAGE_ROWMAX);
+    hipLaunchKernelGGL(krm, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, tilemax);
+    tm.end(EA_STAGE_ROWMAX);
+  }
 
   constexpr int BINS = 16;
   const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)kBQW * (BINS * 2 + 2) * 8 + 4 * kChunk +
