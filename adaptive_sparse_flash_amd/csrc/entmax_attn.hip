@@ -601,9 +601,8 @@ struct TileMaxQueue {
 // rounded up; it bounds tau from below and prunes key tiles that can never
 // hold a nonzero probability).  Each wave
 // owns 64 queries (two B-operand blocks share every K fragment read from
-// LDS); the workgroup (256 queries) streams K tiles through LDS (bf16: three
-// stages filled by direct global->LDS loads; fp32: double-buffered through
-// registers).
+// LDS); the workgroup (256 queries) streams K tiles double-buffered through
+// registers.  This 32x32 form serves fp32 inputs; bf16 runs k_rowmax16.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, const E* __restrict__ K,
                                                      Params P, float* __restrict__ rowmax,
@@ -634,22 +633,12 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
 
   float m[2] = {-INFINITY, -INFINITY};
-  constexpr bool kDirect = sizeof(E) == 2;
-  using DT = DirectTile<D>;
-  constexpr int NS = 3;                          // LDS stages of the direct pipeline
   RowStage<E, D, kBK> st;
-  const DT dt(reinterpret_cast<const __bf16*>(Kh), N, w, lane);
-  if constexpr (kDirect) {
-    // tiles 0 and 1 in flight; each step waits for its own tile only
-    if (0 < kt_end) dt.issue(smem, 0, w);
-    if (1 < kt_end) dt.issue(smem + DT::BYTES, kBK, w);
-  } else {
-    if (kt_end > 0) {
-      st.load(Kh, 0, N);
-      st.store(smem, KS);
-    }
-    __syncthreads();
+  if (kt_end > 0) {
+    st.load(Kh, 0, N);
+    st.store(smem, KS);
   }
+  __syncthreads();
 
   const int ktp = tilemax_row(P.n_kt);
   // d = 128 stores 64-byte segments; d = 64 keeps 16-byte stores, which spares
@@ -658,10 +647,9 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   const int my_row = h ? iq[1] : iq[0];
   TileMaxQueue<kSeg> tq(my_row < N ? tilemax + ((size_t)bh * N + my_row) * ktp : nullptr);
   // one tile: scores for both query blocks, optional masking, maxima
-  int drain = 0;   // steps that wait for every memory operation (after stores)
   auto tile = [&](int kt, auto masked) {
     float tmax[2];
-    const char* kl = kDirect ? smem + (kt % NS) * DT::BYTES : smem + (kt & 1) * kBK * KS;
+    const char* kl = smem + (kt & 1) * kBK * KS;
     f32x16 acc[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
@@ -670,10 +658,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         Frag<E> a;
-        if constexpr (kDirect)
-          ld8(a, DT::at(kl, 32 * kb + c32, 2 * c + h));
-        else
-          ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
+        ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
         mma(acc[0][kb], a, qf[0][c]);
         mma(acc[1][kb], a, qf[1][c]);
       }
@@ -695,41 +680,21 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
     const float r0 = half_swap_max(tmax[0]);
     const float r1 = half_swap_max(tmax[1]);
     tq.push(half_bits_up((h ? r1 : r0) * P.scale));
-    if (tq.tile_done(kt)) drain = NS - 1;
+    tq.tile_done(kt);
   };
 
   int kt = 0;
-  if constexpr (kDirect) {
-    // Step kt: wait for tile kt (tile kt+1 may stay in flight unless stores
-    // were issued since), barrier, refill the stage freed by tile kt-1 with
-    // tile kt+2, compute tile kt.  Bare s_barrier: a full __syncthreads would
-    // wait for every load in flight.
-    auto step = [&](int kt, auto masked, bool compute) {
-      if (drain > 0 || kt + 1 >= kt_end) {
-        wait_vmcnt<0>();
-      } else {
-        wait_vmcnt<DT::NI>();
-      }
-      if (drain > 0) --drain;
-      __builtin_amdgcn_s_barrier();
-      if (kt + 2 < kt_end) dt.issue(smem + ((kt + 2) % NS) * DT::BYTES, (kt + 2) * kBK, w);
-      if (compute) tile(kt, masked);
-    };
-    for (; kt < kt_full; ++kt) step(kt, std::false_type{}, true);
-    for (; kt < kt_end; ++kt) step(kt, std::true_type{}, kt < kt_end_w);
-  } else {
-    for (; kt < kt_full; ++kt) {
-      if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
-      tile(kt, std::false_type{});
-      if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
-      __syncthreads();
-    }
-    for (; kt < kt_end; ++kt) {
-      if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
-      if (kt < kt_end_w) tile(kt, std::true_type{});
-      if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
-      __syncthreads();
-    }
+  for (; kt < kt_full; ++kt) {
+    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
+    tile(kt, std::false_type{});
+    if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
+    __syncthreads();
+  }
+  for (; kt < kt_end; ++kt) {
+    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
+    if (kt < kt_end_w) tile(kt, std::true_type{});
+    if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
+    __syncthreads();
   }
   tq.finish(max(kt_end_w, kt_full));
 #pragma unroll
@@ -749,6 +714,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
 __device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+constexpr int kRowmaxTPS = 2;      // K tiles per barrier step (two steps of slots in LDS)
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict__ Q,
                                                        const __bf16* __restrict__ K, Params P,
@@ -756,7 +722,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
                                                        uint16_t* __restrict__ tilemax) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using DT = DirectTile<D>;
-  constexpr int NS = 3;            // LDS stages
+  constexpr int TPS = kRowmaxTPS;
   constexpr int KST = D / 32;      // contraction steps of 32
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int N = P.N;
@@ -784,17 +750,17 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
   const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
 
   const DT dt(Kh, N, w, lane);
-  if (0 < kt_end) dt.issue(smem, 0, w);
-  if (1 < kt_end) dt.issue(smem + DT::BYTES, kBK, w);
+#pragma unroll
+  for (int j = 0; j < TPS; ++j)
+    if (j < kt_end) dt.issue(smem + j * DT::BYTES, j * kBK, w);
 
   const int ktp = tilemax_row(P.n_kt);
   constexpr int kSeg = D == 64 ? 1 : 4;
   TileMaxQueue<kSeg> tq(iq < N ? tilemax + ((size_t)bh * N + iq) * ktp : nullptr);
   float m = -INFINITY;
-  int drain = 0;
 
   auto tile = [&](int kt, auto masked) {
-    const char* kl = smem + (kt % NS) * DT::BYTES;
+    const char* kl = smem + (kt % (2 * TPS)) * DT::BYTES;
     f32x4 acc[4][4];               // [query block][key block]
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -842,26 +808,30 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
     const float tm = __builtin_elementwise_maximum(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
     m = fmaxf(m, tm);
     tq.push(half_bits_up(tm * P.scale));
-    if (tq.tile_done(kt)) drain = NS - 1;
+    tq.tile_done(kt);
   };
 
-  // Step kt: wait for tile kt (tile kt+1 may stay in flight unless stores
-  // were issued since), bare barrier, refill the stage freed by tile kt-1
-  // with tile kt+2, compute tile kt.
-  auto step = [&](int kt, auto masked, bool compute) {
-    if (drain > 0 || kt + 1 >= kt_end) {
-      wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<DT::NI>();
-    }
-    if (drain > 0) --drain;
+  // Step over TPS tiles: wait for them (issued one step earlier; this also
+  // retires the tile-max stores), bare barrier (a full __syncthreads would add
+  // a memory fence), issue the next step's tiles into the slots that the
+  // previous step read, compute.
+  for (int kt0 = 0; kt0 < kt_end; kt0 += TPS) {
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    if (kt + 2 < kt_end) dt.issue(smem + ((kt + 2) % NS) * DT::BYTES, (kt + 2) * kBK, w);
-    if (compute) tile(kt, masked);
-  };
-  int kt = 0;
-  for (; kt < kt_full; ++kt) step(kt, std::false_type{}, true);
-  for (; kt < kt_end; ++kt) step(kt, std::true_type{}, kt < kt_end_w);
+#pragma unroll
+    for (int j = 0; j < TPS; ++j) {
+      const int kn = kt0 + TPS + j;
+      if (kn < kt_end) dt.issue(smem + (kn % (2 * TPS)) * DT::BYTES, kn * kBK, w);
+    }
+#pragma unroll
+    for (int j = 0; j < TPS; ++j) {
+      const int kt = kt0 + j;
+      if (kt < kt_full)
+        tile(kt, std::false_type{});
+      else if (kt < kt_end_w)
+        tile(kt, std::true_type{});
+    }
+  }
   tq.finish(max(kt_end_w, kt_full));
   if (iq < N) rowmax[(size_t)bh * N + iq] = m * P.scale;
 }
@@ -1925,7 +1895,7 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
 
   constexpr int KS = row_stride<E, D>();
   if constexpr (sizeof(E) == 2) {
-    const size_t rm_lds = (size_t)3 * DirectTile<D>::BYTES;
+    const size_t rm_lds = (size_t)2 * kRowmaxTPS * DirectTile<D>::BYTES;
     auto krm = k_rowmax16<D>;
     if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
     tm.begin(EA_STAGE_ROWMAX);
