@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark: fused alpha-entmax attention, forward + backward, on one MI355X.
 
-One step = the whole hot path over one batch: entmax_attn_fwd (V^T copy, tau
-solve with block mask, P V) followed by entmax_attn_bwd (transposed copies and
-delta, dQ, dK/dV), inputs resident in HBM before timing starts.
+One step = the whole hot path over one batch: entmax_attn_fwd (row and tile
+maxima, tau solve with block mask, P V) followed by entmax_attn_bwd (delta and
+dQ, then dK/dV), inputs resident in HBM before timing starts.
 
 Default workload (the one the headline metric is quoted on): B=1, H=16,
 N=16384, d=128, bf16, causal, alpha=1.5, planted-cluster locality (64 random
@@ -20,8 +20,10 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -33,6 +35,23 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "adaptive_sparse_flash_amd", "csrc", "entmax_attn.hip")
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "k_rowmax16_planted_16k_hbm_counters.md")
+
+
+def recorded_traffic(summary: str = COUNTER_SUMMARY, src: str = KERNEL_SRC):
+    """HBM bytes per row-max launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy), or None when the
+    counters were taken on a different kernel source."""
+    try:
+        text = open(summary).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(\w+) = (\S+)$", text, re.M))
+    if vals.get("kernel_source_sha256") != digest or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
 
 
 def dense_equiv_flops(w) -> float:
@@ -129,6 +148,8 @@ def main():
     ap.add_argument("--strength", type=float, default=None,
                     help="planted workloads: query strength a (Q = a*c + noise); sets the sparsity")
     ap.add_argument("--alpha", type=float, default=None, help="override the workload's alpha")
+    ap.add_argument("--scale", type=float, default=None,
+                    help="iid workloads: standard deviation c of Q and K (sets the sparsity)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 512 MiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -146,6 +167,8 @@ def main():
         over["strength"] = args.strength
     if args.alpha is not None:
         over["alpha"] = args.alpha
+    if args.scale is not None:
+        over["scale"] = args.scale
     w = G.workload(args.workload, **over)
     x = G.make_inputs(w)
     dt_in = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -194,16 +217,19 @@ def main():
     flops = dense_equiv_flops(w)
     value = flops / (ms * 1e-3) / 1e12
 
-    # Dominant kernel: k_rowmax, the one full score sweep.  Its algorithmic
-    # work per launch is 2*d flops per visible score: B*H*N*(N+1)/2 visible
-    # scores when causal, B*H*N^2 otherwise.
+    # Dominant kernel: the row-max sweep (k_rowmax16 for bf16), the one full
+    # score sweep.  Its algorithmic work per launch is 2*d flops per visible
+    # score: B*H*N*(N+1)/2 visible scores when causal, B*H*N^2 otherwise.
     vis = w.N * (w.N + 1) / 2 if w.causal else float(w.N) * w.N
     sweep_flops = 2.0 * w.d * vis * w.B * w.H
     rm_ms = stage_ms["rowmax"]
     achieved = sweep_flops / (rm_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "k_rowmax", "achieved": achieved,
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+    default_config = (args.workload == "planted_16k" and args.strength is None and args.alpha is None
+                      and args.scale is None and args.tau_mode == "hist")
+    roofline = {"bound": "mfma", "kernel": "k_rowmax16" if w.dtype == "bf16" else "k_rowmax",
+                "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                "traffic": recorded_traffic() if default_config else None,
                 "flops_per_launch": sweep_flops, "launch_ms": rm_ms}
 
     line = {

@@ -100,9 +100,10 @@ typedef struct {
 #define EA_NUM_STAGES      7
 
 /* Bytes of device workspace both entry points need for `desc`: one float per
- * row, (forward) one float per block_mask tile, and for fp32 inputs transposed
- * copies of V (forward) or of K, Q, dO (backward).  O(B*H*N*d + B*H*n_qt*n_kt); no
- * N^2-element buffer.  Returns 0 for an invalid desc. */
+ * row; (forward) each row's maximum over every 64-key tile, as a half rounded
+ * up, rows padded to a multiple of 32 tiles (B*H*N*ceil(N/2048)*64 bytes, about
+ * 1/128 of an fp32 score matrix); and for fp32 inputs transposed copies of V
+ * (forward) or of K, Q, dO (backward).  Returns 0 for an invalid desc. */
 size_t entmax_attn_workspace_bytes(const ea_desc* desc);
 
 /* Shape of block_mask: [B, H, n_qt, n_kt] bytes with n_qt = ceil(N/bm),
