@@ -310,14 +310,19 @@ __device__ __forceinline__ void scores_T(f32x16 (&acc)[2], const char* klds, int
   const int c32 = lane & 31, h = lane >> 5;
   acc[0] = f32x16{};
   acc[1] = f32x16{};
+  // K fragments run three MFMA steps ahead of their use, so an LDS read
+  // never stalls the MFMA that consumes it
+  constexpr int kSteps = D / 16 * 2, kAhead = 3;
+  auto addr = [&](int st) {
+    return reinterpret_cast<const E*>(klds + (32 * (st & 1) + c32) * ks) + 16 * (st >> 1) + 8 * h;
+  };
+  Frag<E> a[kAhead + 1];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
+  for (int st = 0; st < kAhead; ++st) ld8(a[st], addr(st));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      Frag<E> a;
-      ld8(a, reinterpret_cast<const E*>(klds + (32 * kb + c32) * ks) + 16 * c + 8 * h);
-      mma(acc[kb], a, qf[c]);
-    }
+  for (int st = 0; st < kSteps; ++st) {
+    if (st + kAhead < kSteps) ld8(a[(st + kAhead) % (kAhead + 1)], addr(st + kAhead));
+    mma(acc[st & 1], a[st % (kAhead + 1)], qf[st >> 1]);
   }
 }
 
@@ -449,6 +454,53 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// ROWS-row tiles of one head's [N][D] matrix staged into LDS rows of
+// row_stride<E, D>() bytes.  fetch(dst, row0) starts the copy of rows
+// row0 .. row0+ROWS-1, commit(dst) finishes it; the tile is complete for the
+// whole workgroup after the next __syncthreads.  Rows past N read as zeros.
+//  - bf16, d = 128: buffer_load_dword ... lds, one instruction per row (64
+//    lanes x 4 B) straight into the padded LDS row; no registers hold the
+//    tile and commit is empty.  The buffer descriptor spans the head's N
+//    rows, so its range check supplies the zeros.
+//  - otherwise through registers (RowStage; a d = 64 bf16 tile needs only 8
+//    of them per thread), commit writes them to LDS.
+template <typename E, int D, int ROWS>
+struct RowTiles {
+  RowStage<E, D, ROWS> st;
+  const E* g;
+  int N;
+  __device__ __forceinline__ RowTiles(const E* head, int n, int, int) : g(head), N(n) {}
+  __device__ __forceinline__ void fetch(char*, int row0) { st.load(g, row0, N); }
+  __device__ __forceinline__ void commit(char* dst) const { st.store(dst, row_stride<E, D>()); }
+};
+template <int ROWS>
+struct RowTiles<__bf16, 128, ROWS> {
+  static constexpr int D = 128;
+  static constexpr int RB = D * 2;                   // bytes of one row in memory
+  static constexpr int RS = row_stride<__bf16, D>(); // bytes of one row in LDS
+  static constexpr int RPW = ROWS / kWaves;          // rows issued by each wave
+  __amdgpu_buffer_rsrc_t rsrc;
+  int w, lane;
+  __device__ __forceinline__ RowTiles(const __bf16* head, int n, int w_, int lane_)
+      : w(__builtin_amdgcn_readfirstlane(w_)), lane(lane_) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(head), (short)0, n * RB, 0x00020000);
+  }
+  // row0 and dst must be the same for the whole wave (they come from LDS
+  // lists, so the compiler is told so: the tile offset goes in an SGPR)
+  __device__ __forceinline__ void fetch(char* dst, int row0) {
+    const int r0 = __builtin_amdgcn_readfirstlane(row0);
+    const uint32_t d0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(dst));
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = w * RPW + r;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(d0 + row * RS), 4, lane * 4,
+          (r0 + row) * RB, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void commit(char*) const {}
+};
 
 // Columns col0..col0+W of a transposed [D][Np] matrix (all in range).
 template <typename E, int D, int W, int NT = kThreads>
@@ -1041,15 +1093,15 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     const float bin_scale = (float)BINS / width;
     for (int base = 0; base < kt_end; base += kChunk) {
       const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
-      RowStage<E, D, kBK> st;
+      RowTiles<E, D, kBK> st(Kh, N, w, lane);
       if (n > 0) {
-        st.load(Kh, (base + list[0]) * kBK, N);
-        st.store(kbuf, KS);
+        st.fetch(kbuf, (base + list[0]) * kBK);
+        st.commit(kbuf);
       }
       __syncthreads();
       for (int i = 0; i < n; ++i) {
         const int kt = base + list[i];
-        if (i + 1 < n) st.load(Kh, (base + list[i + 1]) * kBK, N);
+        if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
         if ((wbits[i] >> w) & 1) {
           auto body = [&](auto masked) {
             f32x16 acc[2];
@@ -1073,7 +1125,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
           else
             body(std::false_type{});
         }
-        if (i + 1 < n) st.store(kbuf + ((i + 1) & 1) * kBK * KS, KS);
+        if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
         __syncthreads();
       }
     }
@@ -1169,15 +1221,15 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
     for (int base = 0; base < kt_end; base += kChunk) {
       const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
-      RowStage<E, D, kBK> st;
+      RowTiles<E, D, kBK> st(Kh, N, w, lane);
       if (n > 0) {
-        st.load(Kh, (base + list[0]) * kBK, N);
-        st.store(kbuf, KS);
+        st.fetch(kbuf, (base + list[0]) * kBK);
+        st.commit(kbuf);
       }
       __syncthreads();
       for (int i = 0; i < n; ++i) {
         const int kt = base + list[i];
-        if (i + 1 < n) st.load(Kh, (base + list[i + 1]) * kBK, N);
+        if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
         if (wave_busy && ((wbits[i] >> w) & 1)) {
           auto body = [&](auto masked) {
             f32x16 acc[2];
@@ -1201,7 +1253,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
           else
             body(std::false_type{});
         }
-        if (i + 1 < n) st.store(kbuf + ((i + 1) & 1) * kBK * KS, KS);
+        if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
         __syncthreads();
       }
     }
@@ -1298,27 +1350,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   auto active = [&](int ww, int kt) -> bool {
     return (qtile * kWaves + ww) < P.n_q32 && mask[(mrow0 + ww) * P.n_kt + kt] != 0;
   };
-  RowStage<E, D, kBK> sk;
-  std::conditional_t<kTr, RowStage<E, D, kBK>, ColStage<E, D, kBK>> sv;
-  auto load = [&](int k0) {
-    sk.load(Kh, k0, N);
-    if constexpr (kTr) sv.load(Vh, k0, N);
-    else sv.load(Vh, P.Np, k0);
+  RowTiles<E, D, kBK> sk(Kh, N, w, lane);
+  RowTiles<E, D, kBK> svr(Vh, N, w, lane);   // bf16 V rows
+  ColStage<E, D, kBK> svc;                    // fp32 V^T columns
+  auto load = [&](int k0, int b) {
+    sk.fetch(kbuf + b * kBK * KS, k0);
+    if constexpr (kTr) svr.fetch(vbuf + b * VT, k0);
+    else svc.load(Vh, P.Np, k0);
   };
   auto store = [&](int b) {
-    sk.store(kbuf + b * kBK * KS, KS);
-    sv.store(vbuf + b * VT, VS);
+    sk.commit(kbuf + b * kBK * KS);
+    if constexpr (kTr) svr.commit(vbuf + b * VT);
+    else svc.store(vbuf + b * VT, VS);
   };
   for (int base = 0; base < P.n_kt; base += kChunk) {
     const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
     if (n > 0) {
-      load((base + list[0]) * kBK);
+      load((base + list[0]) * kBK, 0);
       store(0);
     }
     __syncthreads();
     for (int i = 0; i < n; ++i) {
       const int kt = base + list[i];
-      if (i + 1 < n) load((base + list[i + 1]) * kBK);
+      if (i + 1 < n) load((base + list[i + 1]) * kBK, (i + 1) & 1);
       if ((wbits[i] >> w) & 1) {
         const char* kl = kbuf + (i & 1) * kBK * KS;
         const char* vl = vbuf + (i & 1) * VT;
@@ -1453,20 +1507,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   auto active = [&](int ww, int kt) -> bool {
     return (qtile * kWaves + ww) < P.n_q32 && mask[(mrow0 + ww) * P.n_kt + kt] != 0;
   };
-  RowStage<E, D, kBK> sk, sv;
+  RowTiles<E, D, kBK> sk(K + hoff, N, w, lane), sv(V + hoff, N, w, lane);
   ColStage<E, D, kBK> st;
   for (int pass = 0; pass < 2; ++pass) {
     const bool need_kt = !kTr && pass == 1;
-    auto load = [&](int k0) {
-      sk.load(K + hoff, k0, N);
-      sv.load(V + hoff, k0, N);
+    auto load = [&](int k0, int b) {
+      sk.fetch(kbuf + b * kBK * KS, k0);
+      sv.fetch(vbuf + b * kBK * KS, k0);
       if constexpr (!kTr) {
         if (need_kt) st.load(Kth, P.Np, k0);
       }
     };
     auto store = [&](int b) {
-      sk.store(kbuf + b * kBK * KS, KS);
-      sv.store(vbuf + b * kBK * KS, KS);
+      sk.commit(kbuf + b * kBK * KS);
+      sv.commit(vbuf + b * kBK * KS);
       if constexpr (!kTr) {
         if (need_kt) st.store(tbuf + b * TT, VS);
       }
@@ -1474,13 +1528,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     for (int base = 0; base < P.n_kt; base += kChunk) {
       const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
       if (n > 0) {
-        load((base + list[0]) * kBK);
+        load((base + list[0]) * kBK, 0);
         store(0);
       }
       __syncthreads();
       for (int i = 0; i < n; ++i) {
         const int kt = base + list[i];
-        if (i + 1 < n) load((base + list[i + 1]) * kBK);
+        if (i + 1 < n) load((base + list[i + 1]) * kBK, NB == 2 ? ((i + 1) & 1) : 0);
         if ((wbits[i] >> w) & 1) {
           const int buf = NB == 2 ? (i & 1) : 0;
           const char* kl = kbuf + buf * kBK * KS;
@@ -1626,13 +1680,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     return mask[(mbase + r) * P.n_kt + kt] != 0;
   };
 
-  RowStage<E, D, kBQ> sq, so;
+  RowTiles<E, D, kBQ> sq(Q + hoff, N, w, lane), so(dO + hoff, N, w, lane);
   ColStage<E, D, kBQ> sqt, sot;
   float sta = 0.0f, sde = 0.0f;
-  auto load = [&](int r) {
+  auto load = [&](int r, int b) {
     const int qb0 = r * kBQ;
-    sq.load(Q + hoff, qb0, N);
-    so.load(dO + hoff, qb0, N);
+    char* p = smem + b * STEP;
+    sq.fetch(p, qb0);
+    so.fetch(p + kBQ * KS, qb0);
     if constexpr (!kTr) {
       sqt.load(Qth, P.Np, qb0);
       sot.load(dOth, P.Np, qb0);
@@ -1645,8 +1700,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   };
   auto store = [&](int b) {
     char* p = smem + b * STEP;
-    sq.store(p, KS);
-    so.store(p + kBQ * KS, KS);
+    sq.commit(p);
+    so.commit(p + kBQ * KS);
     if constexpr (!kTr) {
       sqt.store(p + 2 * kBQ * KS, TS);
       sot.store(p + 2 * kBQ * KS + TT, TS);
@@ -1661,14 +1716,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   for (int base = 0; base < P.n_q32; base += kChunk) {
     const int n = build_list(base, min(kChunk, P.n_q32 - base), active, list, wbits, flags, counter);
     if (n > 0) {
-      load(base + list[0]);
+      load(base + list[0], 0);
       store(0);
     }
     __syncthreads();
     for (int i = 0; i < n; ++i) {
       const int r = base + list[i];
       const int qb0 = r * kBQ;
-      if (i + 1 < n) load(base + list[i + 1]);
+      if (i + 1 < n) load(base + list[i + 1], (i + 1) & 1);
       if (wave_keys && ((wbits[i] >> w) & 1)) {
         const char* p = smem + (i & 1) * STEP;
         const char* qtl = p;
