@@ -1632,7 +1632,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 // the B operand runs down the columns of the staged Q / dO tiles (bf16:
 // transposed LDS reads; fp32: staged Q^T / dO^T copies).
 template <typename E, int D, int AK>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 && D == 64 ? 2 : 1, 2))) void k_bwd_dkdv(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) void k_bwd_dkdv(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Qt, const E* __restrict__ dOt,
     const float* __restrict__ tau_in, const float* __restrict__ delta_in,
