@@ -1463,7 +1463,7 @@ __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ in, E* 
 // where dP^T = V dO^T, all in the S^T layout.  bf16 reads the dQ operand
 // down the columns of the staged K tile; fp32 stages K^T too.
 template <typename E, int D, int AK, int NB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 && D == 64 && AK == AK15 ? 2 : 1, 2))) void k_bwd_dq(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 && (D == 128 || AK == AK15) ? 2 : 1, 2))) void k_bwd_dq(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Kt, const float* __restrict__ tau_in,
     const uint8_t* __restrict__ mask, Params P, float* __restrict__ delta_out,
