@@ -136,6 +136,17 @@ def test_edge_lengths(n):
         check_all(w, x, run(w, x))
 
 
+@pytest.mark.parametrize("n", [1, 2, 31, 65, 200, 2111])
+def test_edge_lengths_d128(n):
+    """bf16 d=128 takes the direct global->LDS staging (rows past N read as
+    zeros), the 16x16x32 row-max sweep and segment-wise tile-maxima stores:
+    ragged lengths around one tile, one 32-tile segment and a larger tail."""
+    for causal in (True, False):
+        w = G.workload("planted_16k", H=1, N=n, causal=causal)
+        x = G.make_inputs(w)
+        check_all(w, x, run(w, x))
+
+
 def test_empty_sequence():
     bufs = A.Buffers(1, 1, 0, 64, torch.bfloat16, torch.float32)
     z = torch.empty(1, 1, 0, 64, dtype=torch.bfloat16, device="cuda")
