@@ -22,17 +22,22 @@
 //    are queries, so every lane owns one query and per-row sums of f, f', f''
 //    and histogram updates stay inside the lane; only lanes l and l^32 share
 //    a row.  The same register tile, converted to bf16, is the B operand of
-//    O^T = V^T P^T (keys permuted consistently in V^T), so P never leaves
-//    registers.
+//    O^T = V^T P^T, whose A operand is read down the columns of the staged V
+//    rows with ds_read_b64_tr_b16 (keys permuted consistently), so P never
+//    leaves registers.
 //  * t = clamp((alpha-1)/sqrt(d) * acc - tau, 0, 1) is one v_fma_f32 with the
 //    clamp modifier: tau >= max(x) - 1 keeps every t <= 1.
-//  * The first sweep only takes row maxima (MFMA-bound); it also records the
-//    maximum score of every (wave, key tile).  Tiles whose maximum cannot
-//    exceed the lower bracket end max(x) - 1 can never hold a nonzero
-//    probability, so the histogram and Halley sweeps visit candidate tiles only.
+//  * The first sweep (k_rowmax16 for bf16: 16x16x32 MFMA, sixteen independent
+//    accumulators per wave, K tiles loaded straight into XOR-swizzled LDS)
+//    takes only row maxima and each row's maximum over every 64-key tile.
+//    Tiles whose maximum cannot exceed a row's lower bracket end can never
+//    hold a nonzero probability, so the histogram and Halley sweeps visit
+//    candidate tiles only; the tile maxima also raise the lower bracket end.
 //  * The histogram holds integer moments (count, sum y, sum y^2 of
 //    y = x - lo in 2^-24 fixed point) updated with LDS integer atomics, so it is
 //    deterministic and, for alpha in {1.5, 2}, gives f exactly at bin edges.
+//  * The sparse kernels stage d = 128 bf16 tiles with buffer_load ... lds
+//    (no staging registers) and keep LDS reads several MFMA steps ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
