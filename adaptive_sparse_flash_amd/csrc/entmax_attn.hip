@@ -1514,34 +1514,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   };
   RowTiles<E, D, kBK> sk(K + hoff, N, w, lane), sv(V + hoff, N, w, lane);
   ColStage<E, D, kBK> st;
+  // With one list chunk (n_kt <= kChunk) both passes walk the same list: it
+  // is built once, and the first tile of pass 2 is fetched during the last
+  // tile of pass 1.  Buffer parity then continues across the passes.
+  const bool single = P.n_kt <= kChunk;
+  int n_first = 0;
   for (int pass = 0; pass < 2; ++pass) {
-    const bool need_kt = !kTr && pass == 1;
-    auto load = [&](int k0, int b) {
+    auto load = [&](int ps, int k0, int b) {
       sk.fetch(kbuf + b * kBK * KS, k0);
       sv.fetch(vbuf + b * kBK * KS, k0);
       if constexpr (!kTr) {
-        if (need_kt) st.load(Kth, P.Np, k0);
+        if (ps == 1) st.load(Kth, P.Np, k0);
       }
     };
-    auto store = [&](int b) {
+    auto store = [&](int ps, int b) {
       sk.commit(kbuf + b * kBK * KS);
       sv.commit(vbuf + b * kBK * KS);
       if constexpr (!kTr) {
-        if (need_kt) st.store(tbuf + b * TT, VS);
+        if (ps == 1) st.store(tbuf + b * TT, VS);
       }
     };
+    const bool reuse = single && pass == 1;          // list and first tile are ready
+    const bool hand_over = single && pass == 0;      // fetch pass 2's first tile at the end
     for (int base = 0; base < P.n_kt; base += kChunk) {
-      const int n = build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
-      if (n > 0) {
-        load((base + list[0]) * kBK, 0);
-        store(0);
+      const int n = reuse ? n_first
+                          : build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
+      if (hand_over) n_first = n;
+      const int s0 = reuse ? n_first : 0;            // step index of this pass's first tile
+      if (n > 0 && !reuse) {
+        load(pass, (base + list[0]) * kBK, 0);
+        store(pass, 0);
       }
       __syncthreads();
       for (int i = 0; i < n; ++i) {
         const int kt = base + list[i];
-        if (i + 1 < n) load((base + list[i + 1]) * kBK, NB == 2 ? ((i + 1) & 1) : 0);
+        const int nb = NB == 2 ? ((s0 + i + 1) & 1) : 0;
+        const bool next = i + 1 < n || hand_over;
+        if (i + 1 < n)
+          load(pass, (base + list[i + 1]) * kBK, nb);
+        else if (hand_over)
+          load(1, (base + list[0]) * kBK, nb);
         if ((wbits[i] >> w) & 1) {
-          const int buf = NB == 2 ? (i & 1) : 0;
+          const int buf = NB == 2 ? ((s0 + i) & 1) : 0;
           const char* kl = kbuf + buf * kBK * KS;
           auto body = [&](auto masked) {
             f32x16 sacc[2], pacc[2];
@@ -1598,9 +1612,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
           else
             body(std::false_type{});
         }
-        if (i + 1 < n) {
+        if (next) {
           if (NB == 1) __syncthreads();
-          store(NB == 2 ? ((i + 1) & 1) : 0);
+          store(i + 1 < n ? pass : 1, nb);
         }
         __syncthreads();
       }
