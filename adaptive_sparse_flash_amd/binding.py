@@ -2,8 +2,8 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of libentmax_attn.so.  torch tensors provide device memory and the
-current HIP stream.  There is no CPU fallback: if the library is missing the
-import-time loader raises.
+current HIP stream.  There is no CPU fallback: if the library is missing,
+the first call into it raises FileNotFoundError.
 """
 from __future__ import annotations
 

@@ -147,6 +147,23 @@ def test_edge_lengths_d128(n):
         check_all(w, x, run(w, x))
 
 
+def test_autograd_wrapper():
+    """torch.autograd through entmax_attention gives the library's own
+    forward and gradients (bitwise) and matches the oracle."""
+    w = G.workload("planted_16k", H=2, N=400)
+    x = G.make_inputs(w)
+    q, k, v = (torch.from_numpy(x[n]).to(torch.bfloat16).cuda().requires_grad_() for n in ("q", "k", "v"))
+    do = torch.from_numpy(x["dout"]).to(torch.bfloat16).cuda()
+    out = A.entmax_attention(q, k, v, w.alpha, w.causal)
+    (out.float() * do.float()).sum().backward()
+    ref = run(w, x, out_dtype=torch.bfloat16)
+    np.testing.assert_array_equal(out.detach().float().cpu().numpy(), ref["out"])
+    for name, t in (("dq", q), ("dk", k), ("dv", v)):
+        np.testing.assert_array_equal(t.grad.float().cpu().numpy(), ref[name])
+    out_ref, _ = O.attention_forward(x["q"], x["k"], x["v"], w.alpha, w.causal)
+    PT.check_close("autograd out", out.detach().float().cpu().numpy(), out_ref, 1e-2)
+
+
 def test_empty_sequence():
     bufs = A.Buffers(1, 1, 0, 64, torch.bfloat16, torch.float32)
     z = torch.empty(1, 1, 0, 64, dtype=torch.bfloat16, device="cuda")
