@@ -73,6 +73,7 @@ struct Params {
   int mode, max_iters, flags;
   float tol;
   int out_bf16;
+  int pair_qt;            // row-max sweep: one workgroup per pair of causal query tiles
 };
 
 // ----------------------------------------------------------- fragments ---
@@ -784,113 +785,132 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int N = P.N;
   const int n_qt = (N + 255) / 256;
-  int bh, qtile;
-  map_tile(n_qt, P.BH, P.causal, bh, qtile);
-  const int q0 = qtile * 256;
-  const int wq0 = q0 + 64 * w;
+  // Causal query tile t holds 4 (t + 1) key tiles of work.  With pair_qt a
+  // workgroup takes the pair (n_qt - 1 - t, t), so that every workgroup
+  // sweeps the same number of tiles (the middle tile of an odd count runs
+  // alone); otherwise one tile per workgroup, heaviest first.
+  int bh, unit;
+  map_tile(P.pair_qt ? (n_qt + 1) / 2 : n_qt, P.BH, P.causal && !P.pair_qt, bh, unit);
   const __bf16* Qh = Q + (size_t)bh * N * D;
   const __bf16* Kh = K + (size_t)bh * N * D;
-
-  // B fragments: query wq0 + 16 b + c16, dimensions 32 ks + 8 g ... + 7
-  bf16x8 qf[4][KST];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int qi = wq0 + 16 * b + c16;
-#pragma unroll
-    for (int ks = 0; ks < KST; ++ks)
-      qf[b][ks] = qi < N ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qi * D + 32 * ks + 8 * g)
-                         : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-  const int iq = wq0 + lane;       // the query whose maxima this lane keeps
-  const int kt_end = P.causal ? (min(N - 1, q0 + 255) / kBK + 1) : P.n_kt;
-  const int kt_end_w = wq0 >= N ? 0 : (P.causal ? (min(N - 1, wq0 + 63) / kBK + 1) : P.n_kt);
-  const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
-
   const DT dt(Kh, N, w, lane);
-#pragma unroll
-  for (int j = 0; j < TPS; ++j)
-    if (j < kt_end) dt.issue(smem + j * DT::BYTES, j * kBK, w);
-
   const int ktp = tilemax_row(P.n_kt);
   constexpr int kSeg = D == 64 ? 1 : 4;
-  TileMaxQueue<kSeg> tq(iq < N ? tilemax + ((size_t)bh * N + iq) * ktp : nullptr);
-  float m = -INFINITY;
 
-  auto tile = [&](int kt, auto masked) {
-    const char* kl = smem + (kt % (2 * TPS)) * DT::BYTES;
-    f32x4 acc[4][4];               // [query block][key block]
+  auto sweep = [&](int qtile) {
+    const int q0 = qtile * 256;
+    const int wq0 = q0 + 64 * w;
+    // B fragments: query wq0 + 16 b + c16, dimensions 32 ks + 8 g ... + 7
+    bf16x8 qf[4][KST];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b) {
+      const int qi = wq0 + 16 * b + c16;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) acc[b][kb] = f32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < KST; ++ks)
+        qf[b][ks] = qi < N ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qi * D + 32 * ks + 8 * g)
+                           : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    const int iq = wq0 + lane;       // the query whose maxima this lane keeps
+    const int kt_end = P.causal ? (min(N - 1, q0 + 255) / kBK + 1) : P.n_kt;
+    const int kt_end_w = wq0 >= N ? 0 : (P.causal ? (min(N - 1, wq0 + 63) / kBK + 1) : P.n_kt);
+    const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
+
 #pragma unroll
-    for (int ks = 0; ks < KST; ++ks)
+    for (int j = 0; j < TPS; ++j)
+      if (j < kt_end) dt.issue(smem + j * DT::BYTES, j * kBK, w);
+
+    TileMaxQueue<kSeg> tq(iq < N ? tilemax + ((size_t)bh * N + iq) * ktp : nullptr);
+    float m = -INFINITY;
+
+    auto tile = [&](int kt, auto masked) {
+      const char* kl = smem + (kt % (2 * TPS)) * DT::BYTES;
+      f32x4 acc[4][4];               // [query block][key block]
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(DT::at(kl, 16 * kb + c16, 4 * ks + g));
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[b][kb] = mma16(a, qf[b][ks], acc[b][kb]);
+        for (int kb = 0; kb < 4; ++kb) acc[b][kb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(DT::at(kl, 16 * kb + c16, 4 * ks + g));
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[b][kb] = mma16(a, qf[b][ks], acc[b][kb]);
+        }
+      if constexpr (decltype(masked)::value) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int qi = wq0 + 16 * b + c16;
+          // last visible key of query qi, relative to this lane's first key
+          const int lim = (qi >= N ? -1 : (P.causal ? min(qi, N - 1) : N - 1)) - kt * kBK - 4 * g;
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (16 * kb + i > lim) acc[b][kb][i] = -INFINITY;
+        }
       }
-    if constexpr (decltype(masked)::value) {
+      float pm[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int qi = wq0 + 16 * b + c16;
-        // last visible key of query qi, relative to this lane's first key
-        const int lim = (qi >= N ? -1 : (P.causal ? min(qi, N - 1) : N - 1)) - kt * kBK - 4 * g;
+        float t = __builtin_elementwise_maximum(acc[b][0][0], acc[b][0][1]);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * kb + i > lim) acc[b][kb][i] = -INFINITY;
+          for (int i = (kb == 0 ? 2 : 0); i < 4; ++i) t = __builtin_elementwise_maximum(t, acc[b][kb][i]);
+        pm[b] = t;
+      }
+      // Reduce over the four lane groups and scatter: group g keeps query
+      // block g.  permlane32 swap pairs groups (0,2) and (1,3) for blocks
+      // (0,2) and (1,3); permlane16 swap then pairs (0,1) and (2,3).
+      const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[0]), __float_as_uint(pm[2]), false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[1]), __float_as_uint(pm[3]), false, false);
+      const float a0 = __builtin_elementwise_maximum(__uint_as_float(s02[0]), __uint_as_float(s02[1]));
+      const float a1 = __builtin_elementwise_maximum(__uint_as_float(s13[0]), __uint_as_float(s13[1]));
+      const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
+      const float tm = __builtin_elementwise_maximum(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
+      m = fmaxf(m, tm);
+      tq.push(half_bits_up(tm * P.scale));
+      tq.tile_done(kt);
+    };
+
+    // Step over TPS tiles: wait for them (issued one step earlier; this also
+    // retires the tile-max stores), bare barrier (a full __syncthreads would
+    // add a memory fence), issue the next step's tiles into the slots that
+    // the previous step read, compute.
+    for (int kt0 = 0; kt0 < kt_end; kt0 += TPS) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int j = 0; j < TPS; ++j) {
+        const int kn = kt0 + TPS + j;
+        if (kn < kt_end) dt.issue(smem + (kn % (2 * TPS)) * DT::BYTES, kn * kBK, w);
+      }
+#pragma unroll
+      for (int j = 0; j < TPS; ++j) {
+        const int kt = kt0 + j;
+        if (kt < kt_full)
+          tile(kt, std::false_type{});
+        else if (kt < kt_end_w)
+          tile(kt, std::true_type{});
       }
     }
-    float pm[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      float t = __builtin_elementwise_maximum(acc[b][0][0], acc[b][0][1]);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = (kb == 0 ? 2 : 0); i < 4; ++i) t = __builtin_elementwise_maximum(t, acc[b][kb][i]);
-      pm[b] = t;
-    }
-    // Reduce over the four lane groups and scatter: group g keeps query
-    // block g.  permlane32 swap pairs groups (0,2) and (1,3) for blocks
-    // (0,2) and (1,3); permlane16 swap then pairs (0,1) and (2,3).
-    const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[0]), __float_as_uint(pm[2]), false, false);
-    const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[1]), __float_as_uint(pm[3]), false, false);
-    const float a0 = __builtin_elementwise_maximum(__uint_as_float(s02[0]), __uint_as_float(s02[1]));
-    const float a1 = __builtin_elementwise_maximum(__uint_as_float(s13[0]), __uint_as_float(s13[1]));
-    const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
-    const float tm = __builtin_elementwise_maximum(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
-    m = fmaxf(m, tm);
-    tq.push(half_bits_up(tm * P.scale));
-    tq.tile_done(kt);
+    tq.finish(max(kt_end_w, kt_full));
+    if (iq < N) rowmax[(size_t)bh * N + iq] = m * P.scale;
   };
 
-  // Step over TPS tiles: wait for them (issued one step earlier; this also
-  // retires the tile-max stores), bare barrier (a full __syncthreads would add
-  // a memory fence), issue the next step's tiles into the slots that the
-  // previous step read, compute.
-  for (int kt0 = 0; kt0 < kt_end; kt0 += TPS) {
-    wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int j = 0; j < TPS; ++j) {
-      const int kn = kt0 + TPS + j;
-      if (kn < kt_end) dt.issue(smem + (kn % (2 * TPS)) * DT::BYTES, kn * kBK, w);
-    }
-#pragma unroll
-    for (int j = 0; j < TPS; ++j) {
-      const int kt = kt0 + j;
-      if (kt < kt_full)
-        tile(kt, std::false_type{});
-      else if (kt < kt_end_w)
-        tile(kt, std::true_type{});
+  if (!P.pair_qt) {
+    sweep(unit);
+  } else {
+    const int heavy = n_qt - 1 - unit;
+    sweep(heavy);
+    if (unit != heavy) {
+      // every wave is done with the LDS slots before the next tile's first
+      // loads land in them
+      __builtin_amdgcn_s_barrier();
+      sweep(unit);
     }
   }
-  tq.finish(max(kt_end_w, kt_full));
-  if (iq < N) rowmax[(size_t)bh * N + iq] = m * P.scale;
 }
 
 // ------------------------------------------------------------- k_tau ---
@@ -1922,7 +1942,24 @@ Params make_params(const ea_desc* desc, const Shape& s, float alpha, int causal)
   P.flags = desc->flags;
   P.tol = desc->tol > 0.0f ? desc->tol : 1e-6f;
   P.out_bf16 = desc->out_dtype == EA_BF16 ? 1 : 0;
+  P.pair_qt = 0;
   return P;
+}
+
+// Causal row-max sweep: query tile t costs t + 1 key-tile steps.  When the
+// query tiles fill about two rounds of resident workgroups (two per compute
+// unit), pairing t with n - 1 - t in one workgroup gives one round of equal
+// workgroups and measured 5% faster than the heaviest-first order; at four
+// or more rounds the heaviest-first order balances better by itself, and
+// below two rounds the pairs would leave compute units idle.
+bool pair_query_tiles(const Shape& s, int causal) {
+  if (!causal) return false;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return false;
+  const long tiles = (long)s.n_qt256 * s.BH, slots = 2L * cus;
+  return 2 * tiles > 3 * slots && 2 * tiles <= 5 * slots;
 }
 
 // Records the caller's timing events around one stage (no-op without events).
@@ -1973,7 +2010,9 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
     auto krm = k_rowmax16<D>;
     if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
     tm.begin(EA_STAGE_ROWMAX);
-    hipLaunchKernelGGL(krm, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, tilemax);
+    P.pair_qt = pair_query_tiles(s, P.causal) ? 1 : 0;
+    const int units = P.pair_qt ? (s.n_qt256 + 1) / 2 : s.n_qt256;
+    hipLaunchKernelGGL(krm, dim3(units * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, tilemax);
     tm.end(EA_STAGE_ROWMAX);
   } else {
     const size_t rm_lds = (size_t)2 * kBK * KS;

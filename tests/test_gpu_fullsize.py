@@ -68,3 +68,29 @@ def test_full_size_sampled_heads(case):
     it = bufs.iters.cpu().numpy()
     print(f"  tau sweeps per row: mean {it.mean():.2f}, max {it.max()}", flush=True)
     sys.stdout.flush()
+
+
+def test_row_max_pairs_odd_tile_count():
+    """The causal row-max sweep pairs query tiles (t, n - 1 - t) in one
+    workgroup when the tiles fill about two rounds of the GPU.  N = 16100
+    (63 tiles of 256 queries, the last one ragged, 16 heads) takes that path
+    with the middle tile alone; forward parity on the first and last head."""
+    w = G.workload("planted_16k", N=16100, backward=False)
+    print(f"\n[pairs] B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
+    x = G.make_inputs(w)
+    bufs = A.Buffers(w.B, w.H, w.N, w.d, torch.bfloat16, torch.bfloat16, "hist")
+    dev = [torch.from_numpy(x[n]).to(torch.bfloat16).cuda() for n in ("q", "k", "v")]
+    bufs.forward(dev[0], dev[1], dev[2], w.alpha, w.causal)
+    torch.cuda.synchronize()
+    nh = w.B * w.H
+    flat = lambda t: t.reshape(nh, *t.shape[2:])
+    for hh in (0, nh - 1):
+        sl = slice(hh, hh + 1)
+        q, k, v = (x[n].reshape(nh, w.N, w.d)[sl] for n in ("q", "k", "v"))
+        out_ref, tau_ref = O.attention_forward(q, k, v, w.alpha, w.causal)
+        tau = flat(bufs.tau)[sl].cpu().numpy()
+        PT.check_tau(tau, tau_ref)
+        PT.check_close(f"out[h{hh}]", flat(bufs.out)[sl].float().cpu().numpy(), out_ref, PT.out_tol("bf16"))
+        PT.check_support(q, k, w.alpha, w.causal, tau, tau_ref)
+        margins = O.tile_margins(q, k, w.alpha, w.causal, tau_ref, 32, 64)
+        PT.check_mask(flat(bufs.mask)[sl].cpu().numpy(), margins)
