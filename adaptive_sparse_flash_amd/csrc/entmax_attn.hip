@@ -913,6 +913,70 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
   }
 }
 
+// ---------------------------------------------------------- P V tile ---
+// One key tile of O += P V for the 32 queries of a wave: scores from the
+// staged K tile, p = [x - tau]_+^beta, then P V on MFMA with P as the B
+// operand straight from the score accumulators.  bf16: V is a row-major tile
+// (row stride VS) read down its columns; fp32: V^T columns [D][VS].
+template <typename E, int D, int AK, bool M>
+__device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const char* kl, const char* vl, int VS,
+                                        const Frag<E> (&qf)[D / 16], int lane, int lim, float tau,
+                                        const Params& P) {
+  constexpr bool kTr = sizeof(E) == 2;
+  constexpr int KS = row_stride<E, D>();
+  const int h = lane >> 5, c32 = lane & 31;
+  f32x16 acc[2];
+  tile_scores<E, D>(acc, kl, KS, qf, lane, lim, std::integral_constant<bool, M>{});
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
+      float p, u;
+      Ent<AK>::pu(t, P.beta, p, u);
+      acc[kb][j] = p;
+    }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      Frag<E> pf;
+      from_acc(pf, acc[kb], 8 * s);
+      const int koff = 32 * kb + 16 * s + 4 * h;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        Frag<E> vf;
+        if constexpr (kTr) {
+          ld_col8(vf, vl, VS, koff, 32 * db, lane);
+        } else {
+          const E* vrow = reinterpret_cast<const E*>(vl + (32 * db + c32) * VS);
+          ld4x2(vf, vrow + koff, vrow + koff + 8);
+        }
+        mma(oacc[db], vf, pf);
+      }
+    }
+}
+
+// Writes a wave's O accumulators for query iq (fp32 or bf16 out).
+template <int D>
+__device__ __forceinline__ void store_out(const f32x16 (&oacc)[D / 32], void* out, size_t row, int h,
+                                          bool out_bf16) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * db + 8 * g + 4 * h;
+      const size_t off = row * D + d0;
+      const f32x4 o = f32x4{oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
+      if (out_bf16) {
+        const bf16x4 ob = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + off) = ob;
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = o;
+      }
+    }
+}
+
 // ------------------------------------------------------------- k_tau ---
 // Per workgroup (128 queries, 32 per wave): bracket from the row maxima and
 // the row's tile maxima, candidate key tiles, histogram initialisation,
@@ -922,15 +986,27 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
 // candidate bits u32[4][n_words] | counter.
 constexpr int kChunk = 512;    // key tiles listed at once
 
+template <typename E, int D>
+constexpr int tau_region_bytes(int bins) {
+  // histogram [128][2 bins + 2] u64; for bf16 also the V double buffer of the
+  // P V epilogue, which reuses it
+  return sizeof(E) == 2 && 2 * kBK * row_stride<E, D>() > kBQW * (2 * bins + 2) * 8
+             ? 2 * kBK * row_stride<E, D>()
+             : kBQW * (2 * bins + 2) * 8;
+}
+
 template <typename E, int D, int AK, int BINS>
 __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
+                                                  const E* __restrict__ V,
                                                   const float* __restrict__ rowmax,
                                                   const uint16_t* __restrict__ tilemax, Params P,
                                                   float* __restrict__ tau_out,
                                                   uint8_t* __restrict__ mask_out,
-                                                  uint8_t* __restrict__ iters_out) {
+                                                  uint8_t* __restrict__ iters_out,
+                                                  void* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KS = row_stride<E, D>();
+  constexpr bool kFusePV = sizeof(E) == 2;   // bf16: P V runs here, after tau
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
   int bh, qtile;
@@ -951,11 +1027,12 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   const int n_words = (P.n_kt + 31) >> 5;
   char* kbuf = smem;                                                  // 2 x [64][KS]
   unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem + 2 * kBK * KS);
-  short* list = reinterpret_cast<short*>(hist + kBQW * HROW);
+  short* list = reinterpret_cast<short*>(smem + 2 * kBK * KS + tau_region_bytes<E, D>(BINS));
   uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
   uint8_t* flags = wbits + kChunk;
   uint32_t* cbits = reinterpret_cast<uint32_t*>(flags + kChunk);      // [4][n_words]
   int* counter = reinterpret_cast<int*>(cbits + kWaves * n_words);
+  uint32_t* mbits = reinterpret_cast<uint32_t*>(counter + 16);        // [4][n_words] final mask
 
   const int wq_last = min(N - 1, wq0 + kBQ - 1);
   const int kt_end_w = !wave_rows ? 0 : (P.causal ? wq_last / kBK + 1 : P.n_kt);
@@ -1239,10 +1316,21 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   if (wave_rows) {
     for (int kt = lane; kt < P.n_kt; kt += kWave) mrow[kt] = (dense && kt < kt_end_w) ? 1 : 0;
   }
+  if constexpr (kFusePV) {
+    // the same mask as bits in LDS for the P V epilogue
+    for (int e = lane; e < n_words; e += kWave) {
+      const int nv = min(max(kt_end_w - 32 * e, 0), 32);
+      mbits[w * n_words + e] = dense ? (nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u)) : 0u;
+    }
+  }
   const int max_iters = P.max_iters;
   for (int sweep = 0; sweep <= max_iters + 1; ++sweep) {
     const bool wave_busy = __ballot(!conv) != 0ull;
     if (!__syncthreads_or(wave_busy ? 1 : 0)) break;
+    if (kFusePV && wave_busy && !dense) {
+      // this sweep rewrites the wave's mask
+      for (int e = lane; e < n_words; e += kWave) mbits[w * n_words + e] = 0u;
+    }
     float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
     for (int base = 0; base < kt_end; base += kChunk) {
       const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
@@ -1271,6 +1359,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
             if (!dense) {
               const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
               if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
+              if (kFusePV && any && lane == 0) atomicOr(&mbits[w * n_words + (kt >> 5)], 1u << (kt & 31));
             }
           };
           if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
@@ -1326,6 +1415,54 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   if (valid && h == 0) {
     tau_out[(size_t)bh * N + iq] = tau;
     if (iters_out) iters_out[(size_t)bh * N + iq] = (uint8_t)min(iters, 255);
+  }
+
+  // ---- P V over the active tiles of the final mask (bf16).  Q is still in
+  // registers, tau in a register and the mask in LDS; V tiles take the
+  // histogram's place.
+  if constexpr (kFusePV) {
+    __syncthreads();   // every wave's final mask bits (and the histogram is dead)
+    char* vbuf = reinterpret_cast<char*>(hist);                       // 2 x [64][KS]
+    const E* Vh = V + (size_t)bh * N * D;
+    const float ptau = valid ? tau : INFINITY;
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    auto active = [&](int ww, int kt) -> bool { return (mbits[ww * n_words + (kt >> 5)] >> (kt & 31)) & 1u; };
+    RowTiles<E, D, kBK> sk(Kh, N, w, lane), sv(Vh, N, w, lane);
+    for (int base = 0; base < kt_end; base += kChunk) {
+      const int n = build_list(base, min(kChunk, kt_end - base), active, list, wbits, flags, counter);
+      if (n > 0) {
+        sk.fetch(kbuf, (base + list[0]) * kBK);
+        sv.fetch(vbuf, (base + list[0]) * kBK);
+        sk.commit(kbuf);
+        sv.commit(vbuf);
+      }
+      __syncthreads();
+      for (int i = 0; i < n; ++i) {
+        const int kt = base + list[i];
+        const int nb = (i + 1) & 1;
+        if (i + 1 < n) {
+          sk.fetch(kbuf + nb * kBK * KS, (base + list[i + 1]) * kBK);
+          sv.fetch(vbuf + nb * kBK * KS, (base + list[i + 1]) * kBK);
+        }
+        if ((wbits[i] >> w) & 1) {
+          const char* kl = kbuf + (i & 1) * kBK * KS;
+          const char* vl = vbuf + (i & 1) * kBK * KS;
+          const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
+          if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+            pv_tile<E, D, AK, true>(oacc, kl, vl, KS, qf, lane, lim, ptau, P);
+          else
+            pv_tile<E, D, AK, false>(oacc, kl, vl, KS, qf, lane, lim, ptau, P);
+        }
+        if (i + 1 < n) {
+          sk.commit(kbuf + nb * kBK * KS);
+          sv.commit(vbuf + nb * kBK * KS);
+        }
+        __syncthreads();
+      }
+    }
+    if (valid) store_out<D>(oacc, out, (size_t)bh * N + iq, h, P.out_bf16 != 0);
   }
 }
 
@@ -1401,62 +1538,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       if ((wbits[i] >> w) & 1) {
         const char* kl = kbuf + (i & 1) * kBK * KS;
         const char* vl = vbuf + (i & 1) * VT;
-        auto body = [&](auto masked) {
-          f32x16 acc[2];
-          tile_scores<E, D>(acc, kl, KS, qf, lane, row_limit(kt * kBK, iq, N, P.causal, h), masked);
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-              const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
-              float p, u;
-              Ent<AK>::pu(t, P.beta, p, u);
-              acc[kb][j] = p;
-            }
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              Frag<E> pf;
-              from_acc(pf, acc[kb], 8 * s);
-              const int koff = 32 * kb + 16 * s + 4 * h;
-#pragma unroll
-              for (int db = 0; db < D / 32; ++db) {
-                Frag<E> vf;
-                if constexpr (kTr) {
-                  ld_col8(vf, vl, VS, koff, 32 * db, lane);
-                } else {
-                  const E* vrow = reinterpret_cast<const E*>(vl + (32 * db + c32) * VS);
-                  ld4x2(vf, vrow + koff, vrow + koff + 8);
-                }
-                mma(oacc[db], vf, pf);
-              }
-            }
-        };
+        const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
         if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
-          body(std::true_type{});
+          pv_tile<E, D, AK, true>(oacc, kl, vl, VS, qf, lane, lim, tau, P);
         else
-          body(std::false_type{});
+          pv_tile<E, D, AK, false>(oacc, kl, vl, VS, qf, lane, lim, tau, P);
       }
       if (i + 1 < n) store((i + 1) & 1);
       __syncthreads();
     }
   }
-  if (!valid) return;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d0 = 32 * db + 8 * g + 4 * h;
-      const size_t off = ((size_t)bh * N + iq) * D + d0;
-      const f32x4 o = f32x4{oacc[db][4 * g], oacc[db][4 * g + 1], oacc[db][4 * g + 2], oacc[db][4 * g + 3]};
-      if (P.out_bf16) {
-        const bf16x4 ob = bf16x4{(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + off) = ob;
-      } else {
-        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + off) = o;
-      }
-    }
+  if (valid) store_out<D>(oacc, out, (size_t)bh * N + iq, h, P.out_bf16 != 0);
 }
 
 // --------------------------------------------------------- transposes ---
@@ -2024,21 +2116,23 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   }
 
   constexpr int BINS = 16;
-  const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)kBQW * (BINS * 2 + 2) * 8 + 4 * kChunk +
-                         (size_t)kWaves * ((s.n_kt + 31) / 32) * 4 + 64;
+  const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)tau_region_bytes<E, D>(BINS) + 4 * kChunk +
+                         (size_t)2 * kWaves * ((s.n_kt + 31) / 32) * 4 + 64;
   auto ktau = k_tau<E, D, AK, BINS>;
   if ((rc = set_lds(ktau, tau_lds)) != EA_OK) return rc;
   const dim3 g(s.n_qt128 * s.BH);
-  tm.begin(EA_STAGE_TAU);
-  hipLaunchKernelGGL(ktau, g, dim3(kThreads), tau_lds, st, Q, K, rowmax, tilemax, P, tau, mask, iters);
+  tm.begin(EA_STAGE_TAU);   // bf16: tau, block mask and P V in one kernel
+  hipLaunchKernelGGL(ktau, g, dim3(kThreads), tau_lds, st, Q, K, V, rowmax, tilemax, P, tau, mask, iters, out);
   tm.end(EA_STAGE_TAU);
 
-  constexpr int VT = kTr ? kBK * KS : D * (kBK * (int)sizeof(E) + 16);
-  const size_t pv_lds = (size_t)2 * kBK * KS + (size_t)2 * VT + 4 * kChunk + 16;
-  auto kpv = k_pv<E, D, AK>;
-  if ((rc = set_lds(kpv, pv_lds)) != EA_OK) return rc;
-  tm.begin(EA_STAGE_PV);
-  hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, kTr ? V : Vt, tau, mask, P, out);
+  tm.begin(EA_STAGE_PV);   // empty for bf16 (fused above)
+  if constexpr (!kTr) {
+    constexpr int VT = D * (kBK * (int)sizeof(E) + 16);
+    const size_t pv_lds = (size_t)2 * kBK * KS + (size_t)2 * VT + 4 * kChunk + 16;
+    auto kpv = k_pv<E, D, AK>;
+    if ((rc = set_lds(kpv, pv_lds)) != EA_OK) return rc;
+    hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, Vt, tau, mask, P, out);
+  }
   tm.end(EA_STAGE_PV);
   return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }
