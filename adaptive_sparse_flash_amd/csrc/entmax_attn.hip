@@ -1584,7 +1584,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Kt, const float* __restrict__ tau_in,
     const uint8_t* __restrict__ mask, Params P, float* __restrict__ delta_out,
-    void* __restrict__ dq) {
+    uint8_t* __restrict__ maskT, void* __restrict__ dq) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool kTr = sizeof(E) == 2;
   constexpr int KS = row_stride<E, D>();
@@ -1738,6 +1738,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       if (valid && h == 0) delta_out[(size_t)bh * N + iq] = dlt;
     }
   }
+  // This workgroup's four mask rows, transposed ([kt][32-query row], one
+  // 4-byte word per key tile), for the dK/dV kernel's lists.
+  {
+    const int np = (P.n_q32 + 3) & ~3;
+    for (int kt = threadIdx.x; kt < P.n_kt; kt += kThreads) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww)
+        if (active(ww, kt)) word |= 1u << (8 * ww);
+      *reinterpret_cast<uint32_t*>(maskT + ((size_t)bh * P.n_kt + kt) * np + qtile * kWaves) = word;
+    }
+  }
   if (!valid) return;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
@@ -1762,18 +1774,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 // are computed as S = Q K^T here (lane = key), so P and dS feed the A operand;
 // the B operand runs down the columns of the staged Q / dO tiles (bf16:
 // transposed LDS reads; fp32: staged Q^T / dO^T copies).
+// Pipeline depth of the dK/dV query blocks.  The loop takes any depth with
+// the LDS copy engine (bf16, d = 128), but the compiler waits for every copy
+// in flight before a transposed LDS read, so blocks beyond the next one only
+// cost LDS; one wave per SIMD without spills measured slower as well.
+template <typename E, int D>
+constexpr int kv_stages() { return 2; }
+template <typename E, int D>
+constexpr int kv_step_bytes() {
+  return 2 * kBQ * row_stride<E, D>() + 2 * (sizeof(E) == 2 ? 0 : D * (kBQ * (int)sizeof(E) + 16)) + 2 * kBQ * 4;
+}
+
 template <typename E, int D, int AK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) void k_bwd_dkdv(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const E* __restrict__ Qt, const E* __restrict__ dOt,
     const float* __restrict__ tau_in, const float* __restrict__ delta_in,
-    const uint8_t* __restrict__ mask, Params P, void* __restrict__ dk, void* __restrict__ dv) {
+    const uint8_t* __restrict__ maskT, Params P, void* __restrict__ dk, void* __restrict__ dv) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr bool kTr = sizeof(E) == 2;
+  constexpr bool kDirect = kTr && D == 128;          // LDS copy engine for every staged array
+  constexpr int NS = kv_stages<E, D>();
   constexpr int KS = row_stride<E, D>();
   constexpr int TS = kBQ * (int)sizeof(E) + 16;
   constexpr int TT = kTr ? 0 : D * TS;               // bytes of one staged transposed tile
-  constexpr int STEP = 2 * kBQ * KS + 2 * TT + 2 * kBQ * 4;   // one pipeline buffer
+  constexpr int STEP = kv_step_bytes<E, D>();        // one pipeline buffer
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
   int bh, ktile;
@@ -1787,7 +1812,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const E* dOth = kTr ? nullptr : dOt + (size_t)bh * D * P.Np;
 
   // buffer b: Q rows | dO rows | [Q^T cols | dO^T cols] | tau[32] | delta[32]
-  short* list = reinterpret_cast<short*>(smem + 2 * STEP);
+  short* list = reinterpret_cast<short*>(smem + NS * STEP);
   uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
   uint8_t* flags = wbits + kChunk;
   int* counter = reinterpret_cast<int*>(flags + kChunk);
@@ -1803,60 +1828,103 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     dva[db] = f32x16{};
   }
   const int ktA = (ktile * 128) / kBK, ktB = ktA + 1;
-  const size_t mbase = (size_t)bh * P.n_q32;
-  // waves 0, 1 cover key tile A (64 keys), waves 2, 3 key tile B
+  const int np = (P.n_q32 + 3) & ~3;
+  // waves 0, 1 cover key tile A (64 keys), waves 2, 3 key tile B; the
+  // transposed mask gives each key tile's query rows contiguously
   auto active = [&](int ww, int r) -> bool {
     const int kt = ww < 2 ? ktA : ktB;
     if (kt >= P.n_kt || (ktile * 128 + 32 * ww) >= N) return false;
-    return mask[(mbase + r) * P.n_kt + kt] != 0;
+    return maskT[((size_t)bh * P.n_kt + kt) * np + r] != 0;
   };
 
   RowTiles<E, D, kBQ> sq(Q + hoff, N, w, lane), so(dO + hoff, N, w, lane);
   ColStage<E, D, kBQ> sqt, sot;
+  // per-query tau and delta of a block: copy engine (waves 0 and 1, 32 lanes
+  // each; rows past N read as zeros and are masked by the row limits) or
+  // registers of the first 32 threads
+  __amdgpu_buffer_rsrc_t rs_td = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(w == 0 ? tau_in + (size_t)bh * N : delta_in + (size_t)bh * N), (short)0, N * 4,
+      0x00020000);
   float sta = 0.0f, sde = 0.0f;
   auto load = [&](int r, int b) {
     const int qb0 = r * kBQ;
     char* p = smem + b * STEP;
     sq.fetch(p, qb0);
     so.fetch(p + kBQ * KS, qb0);
-    if constexpr (!kTr) {
-      sqt.load(Qth, P.Np, qb0);
-      sot.load(dOth, P.Np, qb0);
-    }
-    if (threadIdx.x < kBQ) {
-      const int qi = qb0 + threadIdx.x;
-      sta = qi < N ? tau_in[(size_t)bh * N + qi] : INFINITY;
-      sde = qi < N ? delta_in[(size_t)bh * N + qi] : 0.0f;
+    if constexpr (kDirect) {
+      if (w < 2 && lane < kBQ) {
+        const uint32_t d0 = __builtin_amdgcn_readfirstlane(
+            (uint32_t)reinterpret_cast<uintptr_t>(p + 2 * kBQ * KS + 2 * TT + w * kBQ * 4));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs_td, reinterpret_cast<__attribute__((address_space(3))) void*>(d0), 4, lane * 4,
+            __builtin_amdgcn_readfirstlane(qb0 * 4), 0, 0);
+      }
+    } else {
+      if constexpr (!kTr) {
+        sqt.load(Qth, P.Np, qb0);
+        sot.load(dOth, P.Np, qb0);
+      }
+      if (threadIdx.x < kBQ) {
+        const int qi = qb0 + threadIdx.x;
+        sta = qi < N ? tau_in[(size_t)bh * N + qi] : INFINITY;
+        sde = qi < N ? delta_in[(size_t)bh * N + qi] : 0.0f;
+      }
     }
   };
   auto store = [&](int b) {
-    char* p = smem + b * STEP;
-    sq.commit(p);
-    so.commit(p + kBQ * KS);
-    if constexpr (!kTr) {
-      sqt.store(p + 2 * kBQ * KS, TS);
-      sot.store(p + 2 * kBQ * KS + TT, TS);
-    }
-    if (threadIdx.x < kBQ) {
-      float* f = reinterpret_cast<float*>(p + 2 * kBQ * KS + 2 * TT);
-      f[threadIdx.x] = sta;
-      f[kBQ + threadIdx.x] = sde;
+    if constexpr (!kDirect) {
+      char* p = smem + b * STEP;
+      sq.commit(p);
+      so.commit(p + kBQ * KS);
+      if constexpr (!kTr) {
+        sqt.store(p + 2 * kBQ * KS, TS);
+        sot.store(p + 2 * kBQ * KS + TT, TS);
+      }
+      if (threadIdx.x < kBQ) {
+        float* f = reinterpret_cast<float*>(p + 2 * kBQ * KS + 2 * TT);
+        f[threadIdx.x] = sta;
+        f[kBQ + threadIdx.x] = sde;
+      }
     }
   };
+  // copy-engine loads one wave issues per block (Q and dO rows; the tau and
+  // delta loads of waves 0 and 1 come on top, so waiting for this many keeps
+  // on the safe side)
+  constexpr int kPerBlock = 2 * kBQ / kWaves;
 
   for (int base = 0; base < P.n_q32; base += kChunk) {
     const int n = build_list(base, min(kChunk, P.n_q32 - base), active, list, wbits, flags, counter);
-    if (n > 0) {
-      load(base + list[0], 0);
-      store(0);
+    if constexpr (kDirect) {
+#pragma unroll
+      for (int j = 0; j < NS - 1; ++j)
+        if (j < n) load(base + list[j], j);
+    } else {
+      if (n > 0) {
+        load(base + list[0], 0);
+        store(0);
+      }
+      __syncthreads();
     }
-    __syncthreads();
     for (int i = 0; i < n; ++i) {
       const int r = base + list[i];
       const int qb0 = r * kBQ;
-      if (i + 1 < n) load(base + list[i + 1], (i + 1) & 1);
+      int buf;
+      if constexpr (kDirect) {
+        // block i landed (blocks i+1 .. i+NS-2 may still be in flight), then
+        // its slot's previous block is done everywhere and i+NS-1 takes it
+        const int ahead = min(NS - 2, n - 1 - i);
+        if (ahead >= 2) wait_vmcnt<2 * kPerBlock>();
+        else if (ahead == 1) wait_vmcnt<kPerBlock>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (i + NS - 1 < n) load(base + list[i + NS - 1], (i + NS - 1) % NS);
+        buf = i % NS;
+      } else {
+        if (i + 1 < n) load(base + list[i + 1], (i + 1) & 1);
+        buf = i & 1;
+      }
       if (wave_keys && ((wbits[i] >> w) & 1)) {
-        const char* p = smem + (i & 1) * STEP;
+        const char* p = smem + buf * STEP;
         const char* qtl = p;
         const char* otl = p + kBQ * KS;
         const char* qttl = p + 2 * kBQ * KS;
@@ -1920,9 +1988,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
           }
         }
       }
-      if (i + 1 < n) store((i + 1) & 1);
-      __syncthreads();
+      if constexpr (!kDirect) {
+        if (i + 1 < n) store((i + 1) & 1);
+        __syncthreads();
+      }
     }
+    if constexpr (kDirect) __syncthreads();   // the next chunk's list and loads reuse the buffers
   }
   if (!wave_keys) return;
 #pragma unroll
@@ -2002,10 +2073,16 @@ size_t tilemax_bytes(const Shape& s) {
   return align_up((size_t)s.BH * s.N * ktp * sizeof(uint16_t), 256);
 }
 
+// the block mask transposed, [BH][n_kt][n_q32 rounded up to 4] bytes
+size_t maskt_bytes(const Shape& s) {
+  return align_up((size_t)s.BH * s.n_kt * (size_t)((s.n_q32 + 3) & ~3), 256);
+}
+
 size_t workspace_bytes(const Shape& s) {
-  // forward: [V^T] | row maxima | tile maxima;  backward: [K^T | Q^T | dO^T] | delta
+  // forward: [V^T] | row maxima | tile maxima;
+  // backward: [K^T | Q^T | dO^T] | delta | transposed mask
   const size_t fwd = transposed_bytes(s) + row_bytes(s) + tilemax_bytes(s);
-  const size_t bwd = 3 * transposed_bytes(s) + row_bytes(s);
+  const size_t bwd = 3 * transposed_bytes(s) + row_bytes(s) + maskt_bytes(s);
   const size_t ws = bwd > fwd ? bwd : fwd;
   return ws > 256 ? ws : 256;
 }
@@ -2153,6 +2230,7 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
   E* Qt = reinterpret_cast<E*>(w + tb);
   E* dOt = reinterpret_cast<E*>(w + 2 * tb);
   float* delta = reinterpret_cast<float*>(w + 3 * tb);
+  uint8_t* maskT = reinterpret_cast<uint8_t*>(w + 3 * tb + row_bytes(s));
   int rc;
   tm.begin(EA_STAGE_BWD_PREP);
   if constexpr (!kTr) {
@@ -2171,16 +2249,15 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
   if ((rc = set_lds(kdq, dq_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_DQ);
   hipLaunchKernelGGL(kdq, dim3(s.n_qt128 * s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO, Kt, tau, mask,
-                     P, delta, dq);
+                     P, delta, maskT, dq);
   tm.end(EA_STAGE_DQ);
 
-  constexpr int TTq = kTr ? 0 : D * (kBQ * (int)sizeof(E) + 16);
-  const size_t kv_lds = (size_t)2 * (2 * kBQ * KS + 2 * TTq + 2 * kBQ * 4) + 4 * kChunk + 16;
+  const size_t kv_lds = (size_t)kv_stages<E, D>() * kv_step_bytes<E, D>() + 4 * kChunk + 16;
   auto kkv = k_bwd_dkdv<E, D, AK>;
   if ((rc = set_lds(kkv, kv_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_DKDV);
   hipLaunchKernelGGL(kkv, dim3(s.n_kt128 * s.BH), dim3(kThreads), kv_lds, st, Q, K, V, dO, Qt, dOt, tau,
-                     delta, mask, P, dk, dv);
+                     delta, maskT, P, dk, dv);
   tm.end(EA_STAGE_DKDV);
   return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
 }

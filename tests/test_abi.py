@@ -59,7 +59,8 @@ def test_workspace_is_rows_plus_tiles():
         assert ws * 120 < bh * n * n * 4 or n < 4096
         f = A.make_desc(1, bh, n, 128, in_dtype=0)
         tr = _align(bh * 128 * nk * 64 * 4)
-        assert A.entmax_attn_workspace_bytes(f) == max(tr + ws, 3 * tr + _align(bh * n * 4))
+        mt = _align(bh * nk * ((-(-n // 32) + 3) // 4 * 4))      # transposed block mask
+        assert A.entmax_attn_workspace_bytes(f) == max(tr + ws, 3 * tr + _align(bh * n * 4) + mt)
     d = A.make_desc(2, 3, 1000, 64, out_dtype=1)
     assert A.entmax_attn_mask_dims(d) == (32, 16, 32, 64)
 
