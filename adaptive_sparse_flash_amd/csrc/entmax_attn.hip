@@ -38,6 +38,12 @@
 //    deterministic and, for alpha in {1.5, 2}, gives f exactly at bin edges.
 //  * The sparse kernels stage d = 128 bf16 tiles with buffer_load ... lds
 //    (no staging registers) and keep LDS reads several MFMA steps ahead.
+//  * For bf16 the tau kernel ends with the P V pass over its final mask
+//    (kept as bits in LDS), so Q, tau and the mask need no second start-up.
+//  * Causal query tiles of the row-max sweep are paired (t, n - 1 - t) per
+//    workgroup when that evens out the rounds of resident workgroups.
+//  * The dQ kernel leaves the block mask transposed in the workspace, so the
+//    dK/dV kernel reads each key tile's active query rows contiguously.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>

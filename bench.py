@@ -13,8 +13,9 @@ K = c + 0.3 N(0,1), V, dO ~ N(0,1)), seed 0.
 Reported value: dense-equivalent TFLOP/s = 3.5 * 4*B*H*N^2*d*(1/2 causal) per
 step / step time.  The line also carries ms/step, the measured block sparsity
 (32x64 and 128x64 tiles), per-stage times from HIP events recorded by the
-library on the launch stream, the roofline of the dominant kernel and the
-float64 CPU oracle timed on a bounded sample of the same workload.
+library on the launch stream (for bf16 the "tau" stage includes P V, and "pv"
+is empty), the roofline of the dominant kernel and the float64 CPU oracle
+timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 

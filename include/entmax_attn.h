@@ -92,8 +92,9 @@ typedef struct {
 /* Stages, for the timing hook. */
 #define EA_STAGE_FWD_PREP  0   /* forward: V^T copy (fp32 inputs only) */
 #define EA_STAGE_ROWMAX    1   /* forward: the full score sweep (row and tile maxima) */
-#define EA_STAGE_TAU       2   /* forward: histogram and Halley sweeps over candidate tiles, block mask */
-#define EA_STAGE_PV        3   /* forward: O = P V over active tiles */
+#define EA_STAGE_TAU       2   /* forward: histogram and Halley sweeps over candidate tiles, block mask;
+                                  for bf16 inputs also O = P V (one kernel) */
+#define EA_STAGE_PV        3   /* forward: O = P V over active tiles (fp32 inputs; empty for bf16) */
 #define EA_STAGE_BWD_PREP  4   /* backward: K^T, Q^T, dO^T copies (fp32 inputs only) */
 #define EA_STAGE_DQ        5   /* backward: delta, then dQ, over active tiles */
 #define EA_STAGE_DKDV      6   /* backward: dK, dV over active tiles */
@@ -102,8 +103,9 @@ typedef struct {
 /* Bytes of device workspace both entry points need for `desc`: one float per
  * row; (forward) each row's maximum over every 64-key tile, as a half rounded
  * up, rows padded to a multiple of 32 tiles (B*H*N*ceil(N/2048)*64 bytes, about
- * 1/128 of an fp32 score matrix); and for fp32 inputs transposed copies of V
- * (forward) or of K, Q, dO (backward).  Returns 0 for an invalid desc. */
+ * 1/128 of an fp32 score matrix); (backward) the block mask transposed, one
+ * byte per (64-key tile, 32-query row); and for fp32 inputs transposed copies
+ * of V (forward) or of K, Q, dO (backward).  Returns 0 for an invalid desc. */
 size_t entmax_attn_workspace_bytes(const ea_desc* desc);
 
 /* Shape of block_mask: [B, H, n_qt, n_kt] bytes with n_qt = ceil(N/bm),
