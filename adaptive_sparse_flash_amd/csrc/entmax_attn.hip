@@ -1830,8 +1830,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   uint8_t* flags = wbits + kChunk;
   int* counter = reinterpret_cast<int*>(flags + kChunk);
 
-  Frag<E> kf[D / 16], vf[D / 16];
-  load_qfrags<E, D>(kf, K + hoff + (size_t)jk * D, kvalid, h);
+  // bf16, d = 128: the workgroup's 128 K rows stay in LDS (each wave copies
+  // its own 32) and the S products read them from there, which frees 32
+  // VGPRs of K fragments; otherwise K fragments are held in registers.
+  char* klds = smem + NS * STEP + 4 * kChunk + 16;
+  Frag<E> kf[kDirect ? 1 : D / 16], vf[D / 16];
+  if constexpr (kDirect) {
+    RowTiles<E, D, 4 * kBQ> sk(K + hoff, N, w, lane);
+    sk.fetch(klds, ktile * 128);
+  } else {
+    load_qfrags<E, D>(kf, K + hoff + (size_t)jk * D, kvalid, h);
+  }
   load_qfrags<E, D>(vf, V + hoff + (size_t)jk * D, kvalid, h);
 
   f32x16 dka[D / 32], dva[D / 32];
@@ -1950,7 +1959,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         for (int c = 0; c < D / 16; ++c) {
           Frag<E> a, b;
           ld8(a, reinterpret_cast<const E*>(qtl + c32 * KS) + 16 * c + 8 * h);
-          mma(sacc, a, kf[c]);
+          if constexpr (kDirect) {
+            Frag<E> kc;
+            ld8(kc, reinterpret_cast<const E*>(klds + (32 * w + c32) * KS) + 16 * c + 8 * h);
+            mma(sacc, a, kc);
+          } else {
+            mma(sacc, a, kf[c]);
+          }
           ld8(b, reinterpret_cast<const E*>(otl + c32 * KS) + 16 * c + 8 * h);
           mma(pacc, b, vf[c]);
         }
@@ -2265,7 +2280,8 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
                      P, delta, maskT, dq);
   tm.end(EA_STAGE_DQ);
 
-  const size_t kv_lds = (size_t)kv_stages<E, D>() * kv_step_bytes<E, D>() + 4 * kChunk + 16;
+  const size_t kv_lds = (size_t)kv_stages<E, D>() * kv_step_bytes<E, D>() + 4 * kChunk + 16 +
+                        (kTr && D == 128 ? (size_t)4 * kBQ * KS : 0);   // the K rows (bf16, d = 128)
   auto kkv = k_bwd_dkdv<E, D, AK>;
   if ((rc = set_lds(kkv, kv_lds)) != EA_OK) return rc;
   tm.begin(EA_STAGE_DKDV);
