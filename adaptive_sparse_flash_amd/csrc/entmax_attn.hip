@@ -1295,6 +1295,41 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         }
         if (!(t0 >= eb && t0 <= eb1)) t0 = -1.0;
       }
+      if (exact && t0 < 0.0 && cstar > 0.0) {
+        // tau's bin holds elements: f is exact for the bins above it, and the
+        // bin's own cstar elements are replaced by cstar/2 at each of mu - sd
+        // and mu + sd, which keeps their count, sum and sum of squares.  The
+        // model equals f at both edges; its root is the start.
+        const unsigned long long g1 = hr[2 * bstar], g2 = hr[2 * bstar + 1];
+        const double s1b = (double)(g1 & ((1ull << 40) - 1ull)) * inv24;
+        const double s2b = (double)g2 * inv48;
+        const double mu = s1b / cstar;
+        const double sd = sqrt(fmax(s2b / cstar - mu * mu, 0.0));
+        const double p2 = mu + sd;
+        const double q1 = fmin(fmax(mu - sd, eb), eb1), q2 = fmin(fmax(p2, eb), eb1);
+        // segments [eb, q1], [q1, q2], [q2, eb1]: moments of what lies above tau
+        const double segA[3] = {Cs + cstar, Cs + 0.5 * cstar, Cs};
+        const double segB[3] = {S1s + s1b, S1s + 0.5 * cstar * p2, S1s};
+        const double segS[3] = {S2s + s2b, S2s + 0.5 * cstar * p2 * p2, S2s};
+        const double segR[3] = {q1, q2, eb1};
+        double a0 = eb;
+        for (int sg = 0; sg < 3; ++sg) {
+          const double A = segA[sg], B = segB[sg], S = segS[sg], a1 = segR[sg];
+          const double fr = (AK == AK15) ? S - 2.0 * a1 * B + a1 * a1 * A - 1.0 : B - a1 * A - 1.0;
+          if (a1 > a0 && fr <= 0.0) {
+            double t = -1.0;
+            if (AK == AK15) {
+              const double disc = B * B - A * (S - 1.0);
+              if (A > 0.0 && disc >= 0.0) t = (B - sqrt(disc)) / A;
+            } else if (A > 0.0) {
+              t = (B - 1.0) / A;
+            }
+            if (t >= 0.0) t0 = fmin(fmax(t, a0), a1);
+            break;
+          }
+          a0 = fmax(a0, a1);
+        }
+      }
       if (t0 < 0.0) {
         const double den = f_lo - f_hi;
         t0 = den > 0.0 ? eb + (eb1 - eb) * (f_lo / den) : 0.5 * (eb + eb1);
