@@ -983,6 +983,26 @@ __device__ __forceinline__ void store_out(const f32x16 (&oacc)[D / 32], void* ou
     }
 }
 
+// z^beta for z > 0 (0 otherwise), in deriv z^(beta-1): the power of the
+// histogram's estimate for alpha other than 1.5 and 2 (float accuracy is
+// ample for a start value).
+template <int AK>
+__device__ __forceinline__ double model_pow(double z, double beta, double& deriv) {
+  if (!(z > 0.0)) {
+    deriv = 0.0;
+    return 0.0;
+  }
+  if constexpr (AK == AK125) {   // beta = 4
+    const double z2 = z * z;
+    deriv = z2 * z;
+    return z2 * z2;
+  } else {
+    const float l = log2f((float)z);
+    deriv = (double)exp2f((float)(beta - 1.0) * l);
+    return (double)exp2f((float)beta * l);
+  }
+}
+
 // ------------------------------------------------------------- k_tau ---
 // Per workgroup (128 queries, 32 per wave): bracket from the row maxima and
 // the row's tile maxima, candidate key tiles, histogram initialisation,
@@ -1245,6 +1265,28 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
       double f_hi = -1.0;                  // f at the upper edge of the bin under test
       int bstar = 0;
       double f_lo = 0, cstar = 0, Cs = 0, S1s = 0, S2s = 0;
+      // Other alpha (estimate only): the elements of every bin b0.. stand
+      // half at mu - sd and half at mu + sd of their bin, which keeps the
+      // bin's count, sum and sum of squares.  Returns f of that model at t
+      // and its derivative in df.
+      auto model_f = [&](int b0, double t, double& df) -> double {
+        double fv = -1.0;
+        df = 0.0;
+        for (int bb = b0; bb < BINS; ++bb) {
+          const unsigned long long g1 = hr[2 * bb], g2 = hr[2 * bb + 1];
+          const double cc = (double)(g1 >> 40);
+          if (cc > 0) {
+            const double mu = (double)(g1 & ((1ull << 40) - 1ull)) * inv24 / cc;
+            const double sd = sqrt(fmax((double)g2 * inv48 / cc - mu * mu, 0.0));
+            double da, db;
+            const double va = model_pow<AK>(mu + sd - t, beta, da);
+            const double vb = model_pow<AK>(mu - sd - t, beta, db);
+            fv += 0.5 * cc * (va + vb);
+            df -= 0.5 * cc * beta * (da + db);
+          }
+        }
+        return fv;
+      };
       for (int b = BINS - 1; b >= 0; --b) {
         const unsigned long long h1 = hr[2 * b], h2 = hr[2 * b + 1];
         const double cb = (double)(h1 >> 40);
@@ -1258,16 +1300,8 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         } else if (AK == AK20) {
           f = S1n - e * Cn - 1.0;                          // exact at the edge
         } else {
-          // other alpha: each bin's elements stand at their mean (estimate only)
-          f = -1.0;
-          for (int bb = b; bb < BINS; ++bb) {
-            const unsigned long long g1 = hr[2 * bb];
-            const double cc = (double)(g1 >> 40);
-            if (cc > 0) {
-              const double mean = (double)(g1 & ((1ull << 40) - 1ull)) * inv24 / cc;
-              f += cc * pow(fmax(mean - e, 0.0), beta);
-            }
-          }
+          double df;
+          f = model_f(b, e, df);                           // estimate
         }
         if (f >= 0.0 || b == 0) {
           bstar = b;
@@ -1285,6 +1319,23 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
       }
       const double eb = (double)bstar * bw, eb1 = (double)(bstar + 1) * bw;
       double t0 = -1.0;
+      if (!exact) {
+        // Newton on the model from the bin's lower edge: the model is convex
+        // and decreasing, so the steps rise monotonically to its root
+        double t = eb;
+        for (int it2 = 0; it2 < 8; ++it2) {
+          double df;
+          const double fv = model_f(bstar, t, df);
+          if (!(fv > 0.0) || !(df < 0.0)) break;
+          const double tn = fmin(t - fv / df, eb1);
+          if (!(tn > t + 1e-7 * bw)) {
+            t = fmax(t, tn);
+            break;
+          }
+          t = tn;
+        }
+        t0 = t;
+      }
       if (exact && cstar == 0.0 && Cs > 0.0) {
         // the tau bin is empty: the support is exactly the bins above it
         if (AK == AK15) {
