@@ -987,19 +987,19 @@ __device__ __forceinline__ void store_out(const f32x16 (&oacc)[D / 32], void* ou
 // histogram's estimate for alpha other than 1.5 and 2 (float accuracy is
 // ample for a start value).
 template <int AK>
-__device__ __forceinline__ double model_pow(double z, double beta, double& deriv) {
-  if (!(z > 0.0)) {
-    deriv = 0.0;
-    return 0.0;
+__device__ __forceinline__ float model_pow(float z, float beta, float& deriv) {
+  if (!(z > 0.0f)) {
+    deriv = 0.0f;
+    return 0.0f;
   }
   if constexpr (AK == AK125) {   // beta = 4
-    const double z2 = z * z;
+    const float z2 = z * z;
     deriv = z2 * z;
     return z2 * z2;
   } else {
-    const float l = log2f((float)z);
-    deriv = (double)exp2f((float)(beta - 1.0) * l);
-    return (double)exp2f((float)beta * l);
+    const float l = log2f(z);
+    deriv = exp2f((beta - 1.0f) * l);
+    return exp2f(beta * l);
   }
 }
 
@@ -1268,26 +1268,26 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
       // Other alpha (estimate only): the elements of every bin b0.. stand
       // half at mu - sd and half at mu + sd of their bin, which keeps the
       // bin's count, sum and sum of squares.  Returns f of that model at t
-      // and its derivative in df.
-      auto model_f = [&](int b0, double t, double& df) -> double {
-        double fv = -1.0;
-        df = 0.0;
+      // (float: a start value needs no more) and its derivative in df.
+      auto model_f = [&](int b0, float t, float& df) -> float {
+        float fv = -1.0f;
+        df = 0.0f;
         for (int bb = b0; bb < BINS; ++bb) {
           const unsigned long long g1 = hr[2 * bb], g2 = hr[2 * bb + 1];
-          const double cc = (double)(g1 >> 40);
-          if (cc > 0) {
-            const double mu = (double)(g1 & ((1ull << 40) - 1ull)) * inv24 / cc;
-            const double sd = sqrt(fmax((double)g2 * inv48 / cc - mu * mu, 0.0));
-            double da, db;
-            const double va = model_pow<AK>(mu + sd - t, beta, da);
-            const double vb = model_pow<AK>(mu - sd - t, beta, db);
-            fv += 0.5 * cc * (va + vb);
-            df -= 0.5 * cc * beta * (da + db);
+          const float cc = (float)(g1 >> 40);
+          if (cc > 0.0f) {
+            const float mu = (float)((double)(g1 & ((1ull << 40) - 1ull)) * inv24) / cc;
+            const float sd = sqrtf(fmaxf((float)((double)g2 * inv48) / cc - mu * mu, 0.0f));
+            float da, db;
+            const float va = model_pow<AK>(mu + sd - t, P.beta, da);
+            const float vb = model_pow<AK>(mu - sd - t, P.beta, db);
+            fv += 0.5f * cc * (va + vb);
+            df -= 0.5f * cc * P.beta * (da + db);
           }
         }
         return fv;
       };
-      for (int b = BINS - 1; b >= 0; --b) {
+      for (int b = exact ? BINS - 1 : -1; b >= 0; --b) {   // the exact edge values
         const unsigned long long h1 = hr[2 * b], h2 = hr[2 * b + 1];
         const double cb = (double)(h1 >> 40);
         const double s1 = (double)(h1 & ((1ull << 40) - 1ull)) * inv24;
@@ -1297,11 +1297,8 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         double f;
         if (AK == AK15) {
           f = S2n - 2.0 * e * S1n + e * e * Cn - 1.0;      // exact at the edge
-        } else if (AK == AK20) {
-          f = S1n - e * Cn - 1.0;                          // exact at the edge
         } else {
-          double df;
-          f = model_f(b, e, df);                           // estimate
+          f = S1n - e * Cn - 1.0;                          // AK20: exact at the edge
         }
         if (f >= 0.0 || b == 0) {
           bstar = b;
@@ -1317,24 +1314,35 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         S1 = S1n;
         S2 = S2n;
       }
+      if (!exact) {
+        // the model decreases in t: tau's bin by bisection over the edges
+        int blo = 0, bhi = BINS;
+        while (bhi - blo > 1) {
+          const int mid = (blo + bhi) >> 1;
+          float df;
+          if (model_f(mid, (float)(mid * bw), df) >= 0.0f) blo = mid; else bhi = mid;
+        }
+        bstar = blo;
+      }
       const double eb = (double)bstar * bw, eb1 = (double)(bstar + 1) * bw;
       double t0 = -1.0;
       if (!exact) {
         // Newton on the model from the bin's lower edge: the model is convex
         // and decreasing, so the steps rise monotonically to its root
-        double t = eb;
+        float t = (float)eb;
+        const float tmax = (float)eb1, dt = 1e-6f * (float)bw;
         for (int it2 = 0; it2 < 8; ++it2) {
-          double df;
-          const double fv = model_f(bstar, t, df);
-          if (!(fv > 0.0) || !(df < 0.0)) break;
-          const double tn = fmin(t - fv / df, eb1);
-          if (!(tn > t + 1e-7 * bw)) {
-            t = fmax(t, tn);
+          float df;
+          const float fv = model_f(bstar, t, df);
+          if (!(fv > 0.0f) || !(df < 0.0f)) break;
+          const float tn = fminf(t - fv / df, tmax);
+          if (!(tn > t + dt)) {
+            t = fmaxf(t, tn);
             break;
           }
           t = tn;
         }
-        t0 = t;
+        t0 = (double)t;
       }
       if (exact && cstar == 0.0 && Cs > 0.0) {
         // the tau bin is empty: the support is exactly the bins above it
