@@ -1424,6 +1424,27 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     }
   }
   const int max_iters = P.max_iters;
+  // The candidate tiles do not change between refinement sweeps.  When the
+  // workgroup's fit beside the K double buffer in the histogram's space (dead
+  // from here), they are copied once and every sweep reads them in place: no
+  // list rebuild, copy or barrier per tile.
+  constexpr int kResident = 2 + tau_region_bytes<E, D>(BINS) / (kBK * KS);
+  auto slot = [&](int i) -> char* {
+    return i < 2 ? kbuf + i * kBK * KS : reinterpret_cast<char*>(hist) + (i - 2) * kBK * KS;
+  };
+  int n_res = -1;   // resident tile count, or -1: the sweeps stream their tiles
+  if (kt_end <= kChunk) {
+    const int n = build_list(0, kt_end, cand, list, wbits, flags, counter);
+    if (n <= kResident) {
+      RowTiles<E, D, kBK> st(Kh, N, w, lane);
+      for (int i = 0; i < n; ++i) {
+        st.fetch(slot(i), list[i] * kBK);
+        st.commit(slot(i));
+      }
+      __syncthreads();
+      n_res = n;
+    }
+  }
   for (int sweep = 0; sweep <= max_iters + 1; ++sweep) {
     const bool wave_busy = __ballot(!conv) != 0ull;
     if (!__syncthreads_or(wave_busy ? 1 : 0)) break;
@@ -1432,43 +1453,48 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
       for (int e = lane; e < n_words; e += kWave) mbits[w * n_words + e] = 0u;
     }
     float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
-    for (int base = 0; base < kt_end; base += kChunk) {
-      const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
-      RowTiles<E, D, kBK> st(Kh, N, w, lane);
-      if (n > 0) {
-        st.fetch(kbuf, (base + list[0]) * kBK);
-        st.commit(kbuf);
-      }
-      __syncthreads();
-      for (int i = 0; i < n; ++i) {
-        const int kt = base + list[i];
-        if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
-        if (wave_busy && ((wbits[i] >> w) & 1)) {
-          auto body = [&](auto masked) {
-            f32x16 acc[2];
-            tile_scores<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane,
-                              row_limit(kt * kBK, iq, N, P.causal, h), masked);
-            const float before = Ent<AK>::count(F0, F1, F2, cnt);
+    // f, f', f'' terms of key tile kt (staged at kl) and its mask bits
+    auto sweep_tile = [&](int kt, const char* kl) {
+      auto body = [&](auto masked) {
+        f32x16 acc[2];
+        tile_scores<E, D>(acc, kl, KS, qf, lane, row_limit(kt * kBK, iq, N, P.causal, h), masked);
+        const float before = Ent<AK>::count(F0, F1, F2, cnt);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-              for (int j = 0; j < 16; ++j) {
-                const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
-                Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
-              }
-            if (!dense) {
-              const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
-              if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
-              if (kFusePV && any && lane == 0) atomicOr(&mbits[w * n_words + (kt >> 5)], 1u << (kt & 31));
-            }
-          };
-          if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
-            body(std::true_type{});
-          else
-            body(std::false_type{});
+          for (int j = 0; j < 16; ++j) {
+            const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
+            Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
+          }
+        if (!dense) {
+          const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
+          if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
+          if (kFusePV && any && lane == 0) atomicOr(&mbits[w * n_words + (kt >> 5)], 1u << (kt & 31));
         }
-        if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
+      };
+      if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+        body(std::true_type{});
+      else
+        body(std::false_type{});
+    };
+    if (n_res >= 0) {
+      for (int i = 0; i < n_res; ++i)
+        if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(list[i], slot(i));
+    } else {
+      for (int base = 0; base < kt_end; base += kChunk) {
+        const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
+        RowTiles<E, D, kBK> st(Kh, N, w, lane);
+        if (n > 0) {
+          st.fetch(kbuf, (base + list[0]) * kBK);
+          st.commit(kbuf);
+        }
         __syncthreads();
+        for (int i = 0; i < n; ++i) {
+          if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
+          if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(base + list[i], kbuf + (i & 1) * kBK * KS);
+          if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
+          __syncthreads();
+        }
       }
     }
     F0 += __shfl_xor(F0, 32);
