@@ -352,6 +352,32 @@ __device__ __forceinline__ void mask_rows_above(f32x16 (&acc)[2], int lim) {
     for (int i = 0; i < 16; ++i)
       if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) acc[kb][i] = -INFINITY;
 }
+// One 32-key half kb of two S^T-shaped tiles at once: sa from the K rows at kl
+// with the query fragments qf, pa from the rows at vl with the fragments of.
+// The two accumulators are independent MFMA chains, interleaved step by step.
+template <typename E, int D>
+__device__ __forceinline__ void scores_T_half2(f32x16& sa, f32x16& pa, const char* kl, const char* vl, int ks,
+                                               int kb, const Frag<E> (&qf)[D / 16],
+                                               const Frag<E> (&of)[D / 16], int lane) {
+  const int c32 = lane & 31, h = lane >> 5;
+  sa = f32x16{};
+  pa = f32x16{};
+  const int roff = (32 * kb + c32) * ks;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    Frag<E> a, b;
+    ld8(a, reinterpret_cast<const E*>(kl + roff) + 16 * st + 8 * h);
+    ld8(b, reinterpret_cast<const E*>(vl + roff) + 16 * st + 8 * h);
+    mma(sa, a, qf[st]);
+    mma(pa, b, of[st]);
+  }
+}
+// rows (keys) of half kb past the visibility limit of mask_rows_above
+__device__ __forceinline__ void mask_half_rows_above(f32x16& acc, int kb, int lim) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) acc[i] = -INFINITY;
+}
 // Tile of S^T (keys x this wave's 32 queries), masked only when `masked`.
 template <typename E, int D, bool M>
 __device__ __forceinline__ void tile_scores(f32x16 (&acc)[2], const char* kl, int ks,
@@ -1803,39 +1829,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
           const int buf = NB == 2 ? ((s0 + i) & 1) : 0;
           const char* kl = kbuf + buf * kBK * KS;
           auto body = [&](auto masked) {
-            f32x16 sacc[2], pacc[2];
-            tile_scores<E, D>(sacc, kl, KS, qf, lane, row_limit(kt * kBK, iq, N, P.causal, h), masked);
-            scores_T<E, D>(pacc, vbuf + buf * kBK * KS, KS, of, lane);
-            if (pass == 0) {
+            // the tile in two 32-key halves: S and dP of one half (32 VGPRs) are
+            // live at a time, which keeps the kernel's spills (and with them the
+            // scratch reloads that wait for the next tile's copy) down
+            const char* vl = vbuf + buf * kBK * KS;
+            const char* tl = tbuf + buf * TT;
+            const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
 #pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb) {
+              f32x16 sacc, pacc;
+              scores_T_half2<E, D>(sacc, pacc, kl, vl, KS, kb, qf, of, lane);
+              if constexpr (decltype(masked)::value) mask_half_rows_above(sacc, kb, lim);
+              if (pass == 0) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                  const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
+                  const float t = clamp01(fmaf(sacc[j], P.scale, -tau));
                   float p, u;
                   Ent<AK>::pu(t, P.beta, p, u);
-                  num = fmaf(u, pacc[kb][j], num);
+                  num = fmaf(u, pacc[j], num);
                   den += u;
                 }
-            } else {
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
+              } else {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                  const float t = clamp01(fmaf(sacc[kb][j], P.scale, -tau));
+                  const float t = clamp01(fmaf(sacc[j], P.scale, -tau));
                   float p, u;
                   Ent<AK>::pu(t, P.beta, p, u);
-                  sacc[kb][j] = u * (pacc[kb][j] - dlt);
+                  sacc[j] = u * (pacc[j] - dlt);
                 }
-              const char* tl = tbuf + buf * TT;
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                   // dQ = sum_j dS_ij k_j cancels strongly when the supporting keys are
                   // nearly parallel (sum_j dS_ij = 0): dS goes in as a hi/lo bf16 pair.
                   Frag<E> sf, sl;
-                  split_acc(sf, sl, sacc[kb], 8 * s);
+                  split_acc(sf, sl, sacc, 8 * s);
                   const int koff = 32 * kb + 16 * s + 4 * h;
 #pragma unroll
                   for (int db = 0; db < D / 32; ++db) {
@@ -1850,6 +1877,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                     if constexpr (kNeedsLo<E>) mma(gacc[db], kf, sl);
                   }
                 }
+              }
             }
           };
           if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
