@@ -107,6 +107,25 @@ def test_tau_modes_agree(mode):
     check_all(w, x, res)
 
 
+@pytest.mark.parametrize("strength", [0.3, 3.0])
+def test_histogram_start_two_sweeps(strength):
+    """For alpha = 1.5 the histogram gives f exactly at its bin edges, and the
+    start inside tau's bin is the root of a model that keeps the bins above
+    exact and puts the bin's own elements at mean -/+ deviation.  On planted
+    data that leaves at most two refinement sweeps per row (the evaluation at
+    the start and one after a Halley step), at mid sparsity (a = 0.3, where a
+    chord between the edge values needed three) and at the headline strength
+    (a = 3, where most rows need one)."""
+    w = G.workload("planted_16k", H=2, N=2048, strength=strength)
+    x = G.make_inputs(w)
+    res = run(w, x)
+    check_all(w, x, res)
+    it = res["iters"].astype(np.int64)
+    assert it.max() <= 2, np.bincount(it.ravel())
+    if strength >= 1.0:
+        assert it.mean() < 1.5, it.mean()
+
+
 def test_skip_on_off_equal():
     w = G.workload("planted_16k", H=1, N=1100)
     x = G.make_inputs(w)
