@@ -117,21 +117,23 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def cpu_baseline(w, x, heads: int):
-    """Time the float64 oracle (forward + backward) on `heads` heads of the
-    workload on this host's cores and scale to a dense-equivalent rate."""
+def cpu_baseline(w, x, max_heads: int, min_seconds: float = 10.0):
+    """Time the float64 oracle (forward + backward) on whole heads of the
+    workload, one after another on this host's cores, until at least
+    `min_seconds` have been spent or `max_heads` heads are done, and scale to
+    a dense-equivalent rate."""
     from oracle import entmax_oracle as O
 
     cores = len(os.sched_getaffinity(0))
-    sl = slice(0, heads)
-    q = x["q"].reshape(-1, w.N, w.d)[sl]
-    k = x["k"].reshape(-1, w.N, w.d)[sl]
-    v = x["v"].reshape(-1, w.N, w.d)[sl]
-    do = x["dout"].reshape(-1, w.N, w.d)[sl]
-    t0 = time.perf_counter()
-    _, tau = O.attention_forward(q, k, v, w.alpha, w.causal, workers=cores)
-    O.attention_backward(q, k, v, do, w.alpha, w.causal, tau=tau, workers=cores)
-    dt = time.perf_counter() - t0
+    qa, ka, va, da = (x[n].reshape(-1, w.N, w.d) for n in ("q", "k", "v", "dout"))
+    dt, heads = 0.0, 0
+    while heads < min(max_heads, w.B * w.H) and (heads == 0 or dt < min_seconds):
+        sl = slice(heads, heads + 1)
+        t0 = time.perf_counter()
+        _, tau = O.attention_forward(qa[sl], ka[sl], va[sl], w.alpha, w.causal, workers=cores)
+        O.attention_backward(qa[sl], ka[sl], va[sl], da[sl], w.alpha, w.causal, tau=tau, workers=cores)
+        dt += time.perf_counter() - t0
+        heads += 1
     flops = dense_equiv_flops(w) * heads / (w.B * w.H)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 oracle forward+backward on {heads} of {w.B * w.H} heads "
@@ -145,7 +147,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="planted_16k")
     ap.add_argument("--tau-mode", default="hist", choices=["hist", "halley", "bisect"])
-    ap.add_argument("--cpu-heads", type=int, default=1, help="heads the CPU oracle is timed on (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="most heads the CPU oracle is timed on, one after another until 10 s are spent "
+                         "(0 = skip)")
     ap.add_argument("--strength", type=float, default=None,
                     help="planted workloads: query strength a (Q = a*c + noise); sets the sparsity")
     ap.add_argument("--alpha", type=float, default=None, help="override the workload's alpha")

@@ -41,3 +41,17 @@ def test_recorded_traffic_requires_matching_source(tmp_path):
     src.write_bytes(b"changed kernel")
     assert bench.recorded_traffic(str(summ), str(src)) is None
     assert bench.recorded_traffic(str(tmp_path / "missing.md"), str(src)) is None
+
+
+def test_cpu_baseline_sample_is_bounded():
+    """The oracle is timed on whole heads, one after another, until the time
+    floor is reached or the head cap is hit; the reported rate covers exactly
+    the heads that ran."""
+    w = G.workload("iid_causal_4k", B=1, H=3, N=96)
+    x = G.make_inputs(w)
+    one = bench.cpu_baseline(w, x, max_heads=4, min_seconds=0.0)
+    assert "on 1 of 3 heads" in one["sample"] and one["kind"] == "oracle" and one["value"] > 0
+    capped = bench.cpu_baseline(w, x, max_heads=2, min_seconds=1e9)
+    assert "on 2 of 3 heads" in capped["sample"]
+    every = bench.cpu_baseline(w, x, max_heads=10, min_seconds=1e9)
+    assert "on 3 of 3 heads" in every["sample"]
