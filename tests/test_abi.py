@@ -109,3 +109,49 @@ def test_empty_sequence_is_a_no_op():
     st = lib.entmax_attn_fwd(None, None, None, 1.5, 1, None, None, None, None,
                              ctypes.byref(d), None, 0, None)
     assert st == 0
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "entmax_attn.h"
+
+int main(void) {
+  ea_desc d;
+  size_t ws;
+  int st, bad, nq = 0, nk = 0, bm = 0, bn = 0;
+  memset(&d, 0, sizeof d);
+  d.B = 1; d.H = 2; d.N = 1000; d.d = 128;
+  d.in_dtype = EA_BF16; d.out_dtype = EA_F32; d.tau_mode = EA_TAU_HIST_HALLEY;
+  ws = entmax_attn_workspace_bytes(&d);
+  st = entmax_attn_mask_dims(&d, &nq, &nk, &bm, &bn);
+  /* missing tensors: rejected before any device work */
+  bad = entmax_attn_fwd(NULL, NULL, NULL, 1.5f, 0, NULL, NULL, NULL, NULL, &d, NULL, 0, NULL);
+  printf("%lu %d %d %d %d %d %d %s\n", (unsigned long)ws, st, nq, nk, bm, bn, bad,
+         entmax_attn_strerror(bad));
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """The header compiles as strict C99 and a C program links against the
+    library and drives its host-side entry points (no GPU involved)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    lib = A.load_library()
+    libdir = os.path.dirname(Bd.LIB)
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-L", libdir, "-lentmax_attn", "-Wl,-rpath," + libdir,
+                    "-Wl,-rpath-link,/opt/rocm/lib", "-o", str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split(maxsplit=7)
+    desc = Bd.make_desc(1, 2, 1000, 128)
+    assert int(out[0]) == Bd.entmax_attn_workspace_bytes(desc)
+    assert [int(v) for v in out[1:6]] == [0, 32, 16, 32, 64]
+    assert int(out[6]) == -1 and out[7].strip() == lib.entmax_attn_strerror(-1).decode()
