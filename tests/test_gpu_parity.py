@@ -126,6 +126,19 @@ def test_histogram_start_two_sweeps(strength):
         assert it.mean() < 1.5, it.mean()
 
 
+def test_beyond_one_list_chunk():
+    """Rows longer than 512 key tiles (N > 32768): the tau kernel walks its
+    candidate tiles in several list chunks and streams them (no resident
+    tiles), and the dQ kernel builds its tile list anew for its second pass.
+    d = 128 bf16 (the copy-engine path), planted clusters, causal, one head,
+    forward and backward against the oracle on every row."""
+    w = G.workload("planted_32k", H=1, N=33000)
+    print(f"\n[chunks] B={w.B} H={w.H} N={w.N} d={w.d}", flush=True)
+    x = G.make_inputs(w)
+    res = run(w, x)
+    check_all(w, x, res)
+
+
 def test_skip_on_off_equal():
     w = G.workload("planted_16k", H=1, N=1100)
     x = G.make_inputs(w)
