@@ -182,34 +182,6 @@ __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 *
 
 __device__ __forceinline__ float clamp01(float v) { return __builtin_amdgcn_fmed3f(v, 0.0f, 1.0f); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o));
-  return v;
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float lane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-// Maximum over the 64 lanes (wave-uniform result): DPP inside each 16-lane
-// row (xor 1, xor 2, half mirror, mirror), then the four row results.
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));   // row_half_mirror
-  v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror
-  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
-}
-
 // max(x[l], x[l ^ 32]) on every lane, by one v_permlane32_swap
 __device__ __forceinline__ float half_swap_max(float x) {
   const unsigned u = __float_as_uint(x);
@@ -287,33 +259,6 @@ template <> struct Ent<AKGEN> {  // any 1 < alpha < 2
 };
 
 // ------------------------------------------------------- tile staging ---
-// Copy `rows` rows of D elements (global rows row0.., zero past N) into LDS
-// rows of `lstride` bytes, in 16-byte pieces spread over the workgroup.
-template <typename E, int D>
-__device__ __forceinline__ void stage_rows(char* lds, int lstride, const E* g, int row0, int rows,
-                                           int N) {
-  constexpr int CH = D * (int)sizeof(E) / 16;
-  for (int c = threadIdx.x; c < rows * CH; c += kThreads) {
-    int r = c / CH, cc = c - r * CH;
-    int gr = row0 + r;
-    f32x4 val = f32x4{0, 0, 0, 0};
-    if (gr < N)
-      val = *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(g + (size_t)gr * D) + cc * 16);
-    *reinterpret_cast<f32x4*>(lds + r * lstride + cc * 16) = val;
-  }
-}
-// Copy columns col0..col0+W of a transposed [D][Np] matrix into LDS [D][W].
-template <typename E, int D, int W>
-__device__ __forceinline__ void stage_cols(char* lds, int lstride, const E* gt, int Np, int col0) {
-  constexpr int CH = W * (int)sizeof(E) / 16;
-  for (int c = threadIdx.x; c < D * CH; c += kThreads) {
-    int r = c / CH, cc = c - r * CH;
-    f32x4 val = *reinterpret_cast<const f32x4*>(
-        reinterpret_cast<const char*>(gt + (size_t)r * Np + col0) + cc * 16);
-    *reinterpret_cast<f32x4*>(lds + r * lstride + cc * 16) = val;
-  }
-}
-
 // S^T for one wave: 64 keys (LDS rows, stride ks) x the wave's 32 queries
 // (B fragments in registers).  acc[kb] holds keys 32kb.. as rows.
 template <typename E, int D>
