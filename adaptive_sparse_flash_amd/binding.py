@@ -119,8 +119,42 @@ def entmax_attn_mask_dims(desc: EaDesc):
     return tuple(v.value for v in vals)
 
 
+_TORCH_DTYPE = {EA_F32: torch.float32, EA_BF16: torch.bfloat16}
+
+
+def _check_tensors(desc: EaDesc, where: str, **spec) -> None:
+    """Every tensor must hold exactly the elements the descriptor implies, in
+    the descriptor's element type, contiguous, on a GPU: the library receives
+    bare pointers and cannot check what they point to.  None is left to the
+    library's own NULL check."""
+    given = {name: v for name, v in spec.items() if v[0] is not None}
+    for name, (t, numel, dtype) in given.items():
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{where}: {name} must be a torch.Tensor")
+        if t.dtype != dtype:
+            raise ValueError(f"{where}: {name} has dtype {t.dtype}, expected {dtype}")
+        if t.numel() != numel:
+            raise ValueError(f"{where}: {name} has {t.numel()} elements, expected {numel}")
+        if not t.is_contiguous():
+            raise ValueError(f"{where}: {name} must be contiguous")
+    for name, (t, numel, _) in given.items():
+        if numel and not t.is_cuda:
+            raise ValueError(f"{where}: {name} must be a GPU tensor")
+
+
+def _sizes(desc: EaDesc):
+    n_qt, n_kt, _, _ = entmax_attn_mask_dims(desc)
+    rows = desc.B * desc.H * desc.N
+    return rows * desc.d, rows, desc.B * desc.H * n_qt * n_kt
+
+
 def entmax_attn_fwd(q, k, v, alpha, causal, out, tau, block_mask, tau_iters, desc, ws,
                     stream=None) -> None:
+    full, rows, mask = _sizes(desc)
+    ti, to = _TORCH_DTYPE.get(desc.in_dtype), _TORCH_DTYPE.get(desc.out_dtype)
+    _check_tensors(desc, "entmax_attn_fwd", q=(q, full, ti), k=(k, full, ti), v=(v, full, ti),
+                   out=(out, full, to), tau=(tau, rows, torch.float32),
+                   block_mask=(block_mask, mask, torch.uint8), tau_iters=(tau_iters, rows, torch.uint8))
     st = load_library().entmax_attn_fwd(
         _ptr(q), _ptr(k), _ptr(v), float(alpha), int(bool(causal)), _ptr(out), _ptr(tau),
         _ptr(block_mask), _ptr(tau_iters), ctypes.byref(desc), _ptr(ws),
@@ -131,6 +165,12 @@ def entmax_attn_fwd(q, k, v, alpha, causal, out, tau, block_mask, tau_iters, des
 
 def entmax_attn_bwd(q, k, v, alpha, causal, dout, tau, block_mask, dq, dk, dv, desc, ws,
                     stream=None) -> None:
+    full, rows, mask = _sizes(desc)
+    ti, to = _TORCH_DTYPE.get(desc.in_dtype), _TORCH_DTYPE.get(desc.out_dtype)
+    _check_tensors(desc, "entmax_attn_bwd", q=(q, full, ti), k=(k, full, ti), v=(v, full, ti),
+                   dout=(dout, full, ti), tau=(tau, rows, torch.float32),
+                   block_mask=(block_mask, mask, torch.uint8), dq=(dq, full, to), dk=(dk, full, to),
+                   dv=(dv, full, to))
     st = load_library().entmax_attn_bwd(
         _ptr(q), _ptr(k), _ptr(v), float(alpha), int(bool(causal)), _ptr(dout), _ptr(tau),
         _ptr(block_mask), _ptr(dq), _ptr(dk), _ptr(dv), ctypes.byref(desc), _ptr(ws),

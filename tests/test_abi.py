@@ -155,3 +155,31 @@ def test_header_is_plain_c_and_links(tmp_path):
     assert int(out[0]) == Bd.entmax_attn_workspace_bytes(desc)
     assert [int(v) for v in out[1:6]] == [0, 32, 16, 32, 64]
     assert int(out[6]) == -1 and out[7].strip() == lib.entmax_attn_strerror(-1).decode()
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The Python entry points check every tensor against the descriptor
+    (element type, element count, contiguity, device) before the library is
+    called, since the library only sees bare pointers."""
+    import torch
+    d = A.make_desc(1, 2, 100, 64)                       # bf16 in, fp32 out
+    n_qt, n_kt, _, _ = A.entmax_attn_mask_dims(d)
+    full, rows = 2 * 100 * 64, 2 * 100
+    q = torch.zeros(1, 2, 100, 64, dtype=torch.bfloat16)
+    out = torch.zeros(full, dtype=torch.float32)
+    tau = torch.zeros(rows, dtype=torch.float32)
+    mask = torch.zeros(2 * n_qt * n_kt, dtype=torch.uint8)
+    fwd = lambda **kw: Bd.entmax_attn_fwd(kw.get("q", q), q, q, 1.5, 1, kw.get("out", out), tau,
+                                          kw.get("mask", mask), None, d, None)
+    with pytest.raises(ValueError, match="dtype"):
+        fwd(q=q.float())
+    with pytest.raises(ValueError, match="elements"):
+        fwd(out=torch.zeros(full - 1, dtype=torch.float32))
+    with pytest.raises(ValueError, match="elements"):
+        fwd(mask=torch.zeros(2 * n_qt * n_kt + 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="contiguous"):
+        fwd(q=torch.zeros(1, 2, 64, 100, dtype=torch.bfloat16).transpose(2, 3))
+    with pytest.raises(ValueError, match="GPU"):
+        fwd()
+    with pytest.raises(ValueError, match="dtype"):
+        Bd.entmax_attn_bwd(q, q, q, 1.5, 1, q, tau, mask, out, out, out.to(torch.bfloat16), d, None)
