@@ -13,7 +13,10 @@ from .binding import (  # noqa: F401
     entmax_attn_fwd,
     entmax_attn_mask_dims,
     entmax_attn_workspace_bytes,
+    entmax_rows,
+    entmax_transform,
     load_library,
     make_desc,
+    make_rows_desc,
     strerror,
 )

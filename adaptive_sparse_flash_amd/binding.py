@@ -27,6 +27,7 @@ EXPORTED = (
     "entmax_attn_mask_dims",
     "entmax_attn_fwd",
     "entmax_attn_bwd",
+    "entmax_rows",
     "entmax_attn_strerror",
 )
 
@@ -38,6 +39,14 @@ class EaDesc(ctypes.Structure):
         ("tau_mode", ctypes.c_int32), ("max_iters", ctypes.c_int32),
         ("tol", ctypes.c_float), ("flags", ctypes.c_int32),
         ("events", ctypes.POINTER(ctypes.c_void_p)),
+    ]
+
+
+class EaRowsDesc(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("n", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("tau_mode", ctypes.c_int32), ("max_iters", ctypes.c_int32),
+        ("tol", ctypes.c_float),
     ]
 
 
@@ -70,6 +79,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.entmax_attn_fwd.restype = i32
     lib.entmax_attn_bwd.argtypes = [vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, dp, vp, sz, vp]
     lib.entmax_attn_bwd.restype = i32
+    lib.entmax_rows.argtypes = [vp, f32, vp, vp, vp, ctypes.POINTER(EaRowsDesc), vp]
+    lib.entmax_rows.restype = i32
     lib.entmax_attn_strerror.argtypes = [i32]
     lib.entmax_attn_strerror.restype = ctypes.c_char_p
     if path is None:
@@ -177,6 +188,40 @@ def entmax_attn_bwd(q, k, v, alpha, causal, dout, tau, block_mask, dq, dk, dv, d
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     if st != EA_OK:
         raise EntmaxAttnError(st, "entmax_attn_bwd")
+
+
+def make_rows_desc(rows, n, in_dtype=torch.float32, out_dtype=torch.float32, tau_mode="hist", max_iters=0,
+                   tol=0.0) -> EaRowsDesc:
+    mode = TAU_MODES[tau_mode] if isinstance(tau_mode, str) else int(tau_mode)
+    code = lambda dt: _dtype_code(dt) if isinstance(dt, torch.dtype) else int(dt)
+    return EaRowsDesc(int(rows), int(n), code(in_dtype), code(out_dtype), mode, int(max_iters), float(tol))
+
+
+def entmax_rows(s, alpha, p, tau, tau_iters, desc, stream=None) -> None:
+    """Row-wise alpha-entmax of score rows s [rows, n] into p [rows, n], tau [rows]."""
+    ti, to = _TORCH_DTYPE.get(desc.in_dtype), _TORCH_DTYPE.get(desc.out_dtype)
+    full = desc.rows * desc.n
+    _check_tensors(desc, "entmax_rows", s=(s, full, ti), p=(p, full, to), tau=(tau, desc.rows, torch.float32),
+                   tau_iters=(tau_iters, desc.rows, torch.uint8))
+    st = load_library().entmax_rows(_ptr(s), float(alpha), _ptr(p), _ptr(tau), _ptr(tau_iters),
+                                    ctypes.byref(desc), _stream(stream))
+    if st != EA_OK:
+        raise EntmaxAttnError(st, "entmax_rows")
+
+
+def entmax_transform(s, alpha=1.5, tau_mode="hist", out_dtype=None, max_iters=0, tol=0.0):
+    """alpha-entmax over the last axis of s (any leading shape, -inf = masked):
+    returns (p, tau, iterations) computed by the library's row kernel."""
+    n = s.shape[-1]
+    rows = s.numel() // max(n, 1)
+    out_dtype = s.dtype if out_dtype is None else out_dtype
+    desc = make_rows_desc(rows, n, s.dtype, out_dtype, tau_mode, max_iters, tol)
+    s = s.contiguous()
+    p = torch.empty(s.shape, dtype=out_dtype, device=s.device)
+    tau = torch.empty(s.shape[:-1], dtype=torch.float32, device=s.device)
+    iters = torch.empty(s.shape[:-1], dtype=torch.uint8, device=s.device)
+    entmax_rows(s, alpha, p, tau, iters, desc)
+    return p, tau, iters
 
 
 # ------------------------------------------------------ convenience layer ---

@@ -80,6 +80,7 @@ struct Params {
   float tol;
   int out_bf16;
   int pair_qt;            // row-max sweep: one workgroup per pair of causal query tiles
+  int hshift;             // histogram fixed point: y in units of 2^-hshift
 };
 
 // ----------------------------------------------------------- fragments ---
@@ -176,6 +177,23 @@ __device__ __forceinline__ void mma(f32x16& c, const Frag<float>& a, const Frag<
   c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.b[3], b.b[3], c, 0, 0, 0);
 }
 
+// fp32 inputs: scores q.k are summed 16 contraction elements at a time from
+// zero, and the chunk sums in double.  Summing all d products in one fp32
+// accumulator rounds at the magnitude of the largest partial sum; where scores
+// are large and tau lies just below them (clustered keys, |x| near 17 at
+// d = 128) that rounding alone moves t = x - tau, and through it dK, by about
+// the fp32 tolerance.
+__device__ __forceinline__ void mma_chunk64(double (&s)[16], const Frag<float>& a, const Frag<float>& b) {
+  f32x16 t = f32x16{};
+  mma(t, a, b);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) s[j] += (double)t[j];
+}
+__device__ __forceinline__ void round_acc(f32x16& acc, const double (&s)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = (float)s[j];
+}
+
 // Row (M index) held by register i of a 32x32 accumulator in lane-half h;
 // the column (N index) is lane & 31.
 __device__ __forceinline__ int acc_row(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
@@ -265,6 +283,21 @@ template <typename E, int D>
 __device__ __forceinline__ void scores_T(f32x16 (&acc)[2], const char* klds, int ks,
                                          const Frag<E> (&qf)[D / 16], int lane) {
   const int c32 = lane & 31, h = lane >> 5;
+  if constexpr (sizeof(E) == 4) {
+    // fp32: one 32-key half at a time, chunk sums in double
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      double sd[16] = {};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+        Frag<E> a;
+        ld8(a, reinterpret_cast<const E*>(klds + (32 * kb + c32) * ks) + 16 * c + 8 * h);
+        mma_chunk64(sd, a, qf[c]);
+      }
+      round_acc(acc[kb], sd);
+    }
+    return;
+  }
   acc[0] = f32x16{};
   acc[1] = f32x16{};
   // K fragments run three MFMA steps ahead of their use, so an LDS read
@@ -308,14 +341,17 @@ __device__ __forceinline__ void scores_T_half2(f32x16& sa, f32x16& pa, const cha
   sa = f32x16{};
   pa = f32x16{};
   const int roff = (32 * kb + c32) * ks;
+  [[maybe_unused]] double sd[sizeof(E) == 4 ? 16 : 1] = {};
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
     Frag<E> a, b;
     ld8(a, reinterpret_cast<const E*>(kl + roff) + 16 * st + 8 * h);
     ld8(b, reinterpret_cast<const E*>(vl + roff) + 16 * st + 8 * h);
-    mma(sa, a, qf[st]);
+    if constexpr (sizeof(E) == 4) mma_chunk64(sd, a, qf[st]);
+    else mma(sa, a, qf[st]);
     mma(pa, b, of[st]);
   }
+  if constexpr (sizeof(E) == 4) round_acc(sa, sd);
 }
 // rows (keys) of half kb past the visibility limit of mask_rows_above
 __device__ __forceinline__ void mask_half_rows_above(f32x16& acc, int kb, int lim) {
@@ -546,102 +582,83 @@ __device__ __forceinline__ int build_list(int base, int len, Pred pred, short* l
   return *counter;
 }
 
-// Tile maxima are kept as IEEE half bits rounded toward +infinity: the stored
-// value bounds the true maximum from above and the half just below it bounds
-// it from below (strictly), which is all the pruning and the lower bracket
-// end need, at half the bytes of fp32.
-// Row length of the tile maxima: whole 64-byte segments (32 tiles), written
-// by one lane at once so that no partial segment reaches memory.
-__host__ __device__ constexpr int tilemax_row(int n_kt) { return (n_kt + 31) & ~31; }
+// Block codes.  For each 32-query block and 64-key tile the row-max sweep
+// keeps one byte c = floor(-128 r), clamped to 0..255, of
+//   r = max over the block's rows i of (M_it - m_i(t))   (x-domain),
+// where M_it is row i's largest score in tile t and m_i(t) the row's running
+// maximum once tile t has been seen.  Since m_i(t) <= max_j x_ij, -c/128 >= r
+// bounds M_it - max_j x_ij from above for every row of the block: a tile whose
+// code gives -c/128 <= min_i (lo_i - max_j x_ij) cannot hold an x_ij above the
+// lower bracket end lo_i of any of the block's rows, so it holds no nonzero
+// probability.  The sweep visits the diagonal (masked) key tiles of a query
+// tile first, where the running maximum of a causal row usually settles, then
+// the rest in order.  One byte per mask entry: the workspace grows like the
+// block mask, not like the score matrix.  Rows are padded to 64 tiles.
+__host__ __device__ constexpr int blk_row(int n_kt) { return (n_kt + 63) & ~63; }
 
-__device__ __forceinline__ uint16_t half_bits_up(float x) {
-  const _Float16 hx = (_Float16)x;
-  uint16_t b = __builtin_bit_cast(uint16_t, hx);
-  if ((float)hx < x) b = (b & 0x8000u) ? (uint16_t)(b - 1u) : (uint16_t)(b + 1u);
-  return b;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float half_up_value(uint16_t b) {
-  return (float)__builtin_bit_cast(_Float16, b);
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// maximum over each 32-lane half of the wave (every lane of the half gets it)
+__device__ __forceinline__ float half_max32(float v) {
+  v = fmax_nan(v, dpp_f<0xB1>(v));     // quad_perm [1,0,3,2]
+  v = fmax_nan(v, dpp_f<0x4E>(v));     // quad_perm [2,3,0,1]
+  v = fmax_nan(v, dpp_f<0x141>(v));    // row_half_mirror
+  v = fmax_nan(v, dpp_f<0x140>(v));    // row_mirror
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_nan(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
-// the half just below the stored one (-inf stays -inf)
-__device__ __forceinline__ float half_down_value(uint16_t b) {
-  uint16_t d;
-  if (b == 0xFC00u) d = b;
-  else if (b == 0x0000u || b == 0x8000u) d = 0x8001u;
-  else d = (b & 0x8000u) ? (uint16_t)(b + 1u) : (uint16_t)(b - 1u);
-  return (float)__builtin_bit_cast(_Float16, d);
+__device__ __forceinline__ float half_min32(float v) { return -half_max32(-v); }
+
+// code of a block's relative maximum r <= 0 (-inf: no visible entry -> 255)
+__device__ __forceinline__ uint32_t blk_code(float r) {
+  return (uint32_t)fminf(floorf(fmaxf(-128.0f * r, 0.0f)), 255.0f);
 }
 
-// Each lane collects one row's tile maxima as half bits: the last 8 in a
-// 16-byte shift register (oldest lowest), groups of 8 in a SEG-deep queue, and
-// stores 8 SEG tiles (16 SEG bytes) at once at the row's position in
-// tilemax[bh][row][kt].  Nothing is stored for rows past N (row_ptr null).
-template <int SEG>
-struct TileMaxQueue {
-  static constexpr uint32_t kNegInf2 = 0xFC00FC00u;   // two half -inf
-  u32x4 tbuf;
-  u32x4 gq[SEG];
-  uint16_t* row_ptr;
-  __device__ __forceinline__ explicit TileMaxQueue(uint16_t* p) : row_ptr(p) {
-    tbuf = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
-#pragma unroll
-    for (int i = 0; i < SEG; ++i) gq[i] = tbuf;
+// Collects one lane's block codes for 32 consecutive tiles: lane l keeps tile
+// (32 s + (l & 31)) of the block (l >> 5 in the 16x16 sweep, the lane half in
+// the 32x32 one) and a segment of 32 bytes is stored at once.  The diagonal
+// tiles [kt_full, kt_end) of a query tile lie in one segment (kt_full is a
+// multiple of 4, at most 4 of them); their codes wait in `vd` until the
+// in-order walk reaches that segment (or are stored at the end).
+struct BlkCodes {
+  uint8_t* row;      // this lane's block row, null when the block is past N
+  int lane32, segd;
+  uint32_t v, vd;
+  bool diag;
+  __device__ __forceinline__ BlkCodes(uint8_t* r, int lane, int kt_full, int kt_end)
+      : row(r), lane32(lane & 31), segd(kt_full >> 5), v(255u), vd(255u), diag(kt_end > kt_full) {}
+  __device__ __forceinline__ void put_diag(int kt, float r) {
+    if ((kt & 31) == lane32) vd = blk_code(r);
   }
-  __device__ __forceinline__ void push(uint32_t hb) {
-    tbuf[0] = __builtin_amdgcn_alignbit(tbuf[1], tbuf[0], 16);
-    tbuf[1] = __builtin_amdgcn_alignbit(tbuf[2], tbuf[1], 16);
-    tbuf[2] = __builtin_amdgcn_alignbit(tbuf[3], tbuf[2], 16);
-    tbuf[3] = __builtin_amdgcn_alignbit(hb, tbuf[3], 16);
+  // in-order tile kt < kt_full (r: the block's value; skipped tiles pass -inf)
+  __device__ __forceinline__ void put(int kt, float r, int kt_full) {
+    if ((kt & 31) == 0) v = ((kt >> 5) == segd) ? vd : 255u;
+    if ((kt & 31) == lane32) v = blk_code(r);
+    if ((kt & 31) == 31 || kt == kt_full - 1) store(kt & ~31, v);
   }
-  __device__ __forceinline__ void push_group() {
-#pragma unroll
-    for (int i = 0; i + 1 < SEG; ++i) gq[i] = gq[i + 1];
-    gq[SEG - 1] = tbuf;
+  __device__ __forceinline__ void store(int kt0, uint32_t val) const {
+    if (row) row[kt0 + lane32] = (uint8_t)val;
   }
-  __device__ __forceinline__ void flush(int kt0) {
-    if (row_ptr) {
-      u32x4* dst = reinterpret_cast<u32x4*>(row_ptr + kt0);
-#pragma unroll
-      for (int i = 0; i < SEG; ++i) dst[i] = gq[i];
-    }
-  }
-  // after tile kt's value was pushed; returns true when it stored a segment
-  __device__ __forceinline__ bool tile_done(int kt) {
-    if ((kt & 7) != 7) return false;
-    push_group();
-    if (((kt >> 3) % SEG) != SEG - 1) return false;
-    flush(kt + 1 - 8 * SEG);
-    return true;
-  }
-  // the last, partial segment after n_done tiles (the rest of it reads -inf)
-  __device__ __forceinline__ void finish(int n_done) {
-    if (n_done % (8 * SEG) == 0) return;
-    if (n_done & 7) {
-      for (int r = n_done & 7; r < 8; ++r) push(0xFC00u);
-      push_group();
-    }
-    const int filled = ((n_done + 7) >> 3) % SEG;   // groups queued in the segment
-    if (filled) {
-      tbuf = u32x4{kNegInf2, kNegInf2, kNegInf2, kNegInf2};
-      for (int g = filled; g < SEG; ++g) push_group();
-    }
-    flush(n_done / (8 * SEG) * (8 * SEG));
+  // after the walk: the diagonal segment, if the in-order walk never reached it
+  __device__ __forceinline__ void finish(int kt_full) const {
+    if (diag && (kt_full == 0 || ((kt_full - 1) >> 5) != segd)) store(segd << 5, vd);
   }
 };
 
 // ---------------------------------------------------------- k_rowmax ---
 // The one full score sweep: per-row maxima of x = (alpha-1) q.k / sqrt(d)
-// and, for every row and 64-key tile, the row's maximum x over the tile
-// (tilemax[bh][row][kt], rows padded to a multiple of 32 tiles, as half bits
-// rounded up; it bounds tau from below and prunes key tiles that can never
-// hold a nonzero probability).  Each wave
-// owns 64 queries (two B-operand blocks share every K fragment read from
+// and the block codes (above) of every 32-query block and 64-key tile.  Each
+// wave owns 64 queries (two B-operand blocks share every K fragment read from
 // LDS); the workgroup (256 queries) streams K tiles double-buffered through
-// registers.  This 32x32 form serves fp32 inputs; bf16 runs k_rowmax16.
+// registers, the diagonal tiles first.  This 32x32 form serves fp32 inputs;
+// bf16 runs k_rowmax16.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, const E* __restrict__ K,
                                                      Params P, float* __restrict__ rowmax,
-                                                     uint16_t* __restrict__ tilemax) {
+                                                     uint8_t* __restrict__ blkc) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KS = row_stride<E, D>();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
@@ -664,79 +681,91 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   const int kt_end = P.causal ? (min(N - 1, q0 + 255) / kBK + 1) : P.n_kt;
   const int kt_end_w = wq0 >= N ? 0 : (P.causal ? (min(N - 1, wq0 + 63) / kBK + 1) : P.n_kt);
   // Tiles below kt_full are fully visible to every query of the workgroup and
-  // lie inside [0, N): they need no masking.  Only the diagonal / tail tiles do.
+  // lie inside [0, N): they need no masking.  Only the diagonal / tail tiles
+  // [kt_full, kt_end) do; they are swept first.
   const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
+  const int n_steps = kt_end;
+  auto tile_at = [&](int s) { return s < kt_end - kt_full ? kt_full + s : s - (kt_end - kt_full); };
 
-  float m[2] = {-INFINITY, -INFINITY};
+  float mr[2] = {-INFINITY, -INFINITY};    // running row maxima (raw q.k)
   RowStage<E, D, kBK> st;
-  if (kt_end > 0) {
-    st.load(Kh, 0, N);
+  if (n_steps > 0) {
+    st.load(Kh, tile_at(0) * kBK, N);
     st.store(smem, KS);
   }
   __syncthreads();
 
-  const int ktp = tilemax_row(P.n_kt);
-  // d = 128 stores 64-byte segments; d = 64 keeps 16-byte stores, which spares
-  // the registers of a third wave per SIMD
-  constexpr int kSeg = D == 64 ? 1 : 4;
-  const int my_row = h ? iq[1] : iq[0];
-  TileMaxQueue<kSeg> tq(my_row < N ? tilemax + ((size_t)bh * N + my_row) * ktp : nullptr);
-  // one tile: scores for both query blocks, optional masking, maxima
-  auto tile = [&](int kt, auto masked) {
-    float tmax[2];
-    const char* kl = smem + (kt & 1) * kBK * KS;
+  // lane half h keeps the codes of query block h (rows wq0 + 32 h ...)
+  const int my_blk = (wq0 >> 5) + h;
+  BlkCodes bc(32 * my_blk < N ? blkc + ((size_t)bh * P.n_q32 + my_blk) * blk_row(P.n_kt) : nullptr, lane,
+              kt_full, kt_end);
+  // one tile: scores for both query blocks, optional masking, maxima; returns
+  // the value of this lane's block for the block codes
+  auto tile = [&](int s, int kt, auto masked) -> float {
+    const char* kl = smem + (s & 1) * kBK * KS;
     f32x16 acc[2][2];
+    if constexpr (sizeof(E) == 4) {
+      // fp32: one (query block, key half) at a time, chunk sums in double
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
+        for (int kb = 0; kb < 2; ++kb) {
+          double sd[16] = {};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        Frag<E> a;
-        ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
-        mma(acc[0][kb], a, qf[0][c]);
-        mma(acc[1][kb], a, qf[1][c]);
+          for (int c = 0; c < D / 16; ++c) {
+            Frag<E> a;
+            ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
+            mma_chunk64(sd, a, qf[qb][c]);
+          }
+          round_acc(acc[qb][kb], sd);
+        }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          Frag<E> a;
+          ld8(a, reinterpret_cast<const E*>(kl + (32 * kb + c32) * KS) + 16 * c + 8 * h);
+          mma(acc[0][kb], a, qf[0][c]);
+          mma(acc[1][kb], a, qf[1][c]);
+        }
       }
     }
+    float rel[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       if constexpr (decltype(masked)::value) mask_rows_above(acc[qb], row_limit(kt * kBK, iq[qb], N, P.causal, h));
       // NaN-propagating maximum: v_maximum3_f32 with no canonicalising of the
       // MFMA results that fmaxf would need
-      float tm = __builtin_elementwise_maximum(acc[qb][0][0], acc[qb][1][0]);
+      float tm = fmax_nan(acc[qb][0][0], acc[qb][1][0]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i)
-        tm = __builtin_elementwise_maximum(tm, __builtin_elementwise_maximum(acc[qb][0][i], acc[qb][1][i]));
-      m[qb] = fmaxf(m[qb], tm);
-      tmax[qb] = tm;
+      for (int i = 1; i < 16; ++i) tm = fmax_nan(tm, fmax_nan(acc[qb][0][i], acc[qb][1][i]));
+      // the row's maximum over the tile (lanes l and l^32 hold its two halves)
+      tm = half_swap_max(tm);
+      mr[qb] = fmaxf(mr[qb], tm);
+      rel[qb] = tm == -INFINITY ? -INFINITY : (tm - mr[qb]) * P.scale;
     }
-    // each row's maximum over the tile (lanes l and l^32 hold its two
-    // halves); lane half h stores the value of query block h
-    const float r0 = half_swap_max(tmax[0]);
-    const float r1 = half_swap_max(tmax[1]);
-    tq.push(half_bits_up((h ? r1 : r0) * P.scale));
-    tq.tile_done(kt);
+    return half_max32(h ? rel[1] : rel[0]);
   };
 
-  int kt = 0;
-  for (; kt < kt_full; ++kt) {
-    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
-    tile(kt, std::false_type{});
-    if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
+  for (int s = 0; s < n_steps; ++s) {
+    const int kt = tile_at(s);
+    if (s + 1 < n_steps) st.load(Kh, tile_at(s + 1) * kBK, N);
+    if (kt >= kt_full) {
+      const float r = kt < kt_end_w ? tile(s, kt, std::true_type{}) : -INFINITY;
+      bc.put_diag(kt, r);
+    } else {
+      bc.put(kt, tile(s, kt, std::false_type{}), kt_full);
+    }
+    if (s + 1 < n_steps) st.store(smem + ((s + 1) & 1) * kBK * KS, KS);
     __syncthreads();
   }
-  for (; kt < kt_end; ++kt) {
-    if (kt + 1 < kt_end) st.load(Kh, (kt + 1) * kBK, N);
-    if (kt < kt_end_w) tile(kt, std::true_type{});
-    if (kt + 1 < kt_end) st.store(smem + ((kt + 1) & 1) * kBK * KS, KS);
-    __syncthreads();
-  }
-  tq.finish(max(kt_end_w, kt_full));
+  bc.finish(kt_full);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float mm = fmaxf(m[qb], __shfl_xor(m[qb], 32));
-    if (iq[qb] < N && h == 0) rowmax[(size_t)bh * N + iq[qb]] = mm * P.scale;
-  }
+  for (int qb = 0; qb < 2; ++qb)
+    if (iq[qb] < N && h == 0) rowmax[(size_t)bh * N + iq[qb]] = mr[qb] * P.scale;
 }
 
 // The same sweep for bf16 inputs on 16x16x32 MFMA: sixteen independent
@@ -754,7 +783,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict__ Q,
                                                        const __bf16* __restrict__ K, Params P,
                                                        float* __restrict__ rowmax,
-                                                       uint16_t* __restrict__ tilemax) {
+                                                       uint8_t* __restrict__ blkc) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using DT = DirectTile<D>;
   constexpr int TPS = kRowmaxTPS;
@@ -771,8 +800,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
   const __bf16* Qh = Q + (size_t)bh * N * D;
   const __bf16* Kh = K + (size_t)bh * N * D;
   const DT dt(Kh, N, w, lane);
-  const int ktp = tilemax_row(P.n_kt);
-  constexpr int kSeg = D == 64 ? 1 : 4;
+  const int ktc = blk_row(P.n_kt);
 
   auto sweep = [&](int qtile) {
     const int q0 = qtile * 256;
@@ -787,20 +815,26 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
         qf[b][ks] = qi < N ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qi * D + 32 * ks + 8 * g)
                            : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    const int iq = wq0 + lane;       // the query whose maxima this lane keeps
     const int kt_end = P.causal ? (min(N - 1, q0 + 255) / kBK + 1) : P.n_kt;
     const int kt_end_w = wq0 >= N ? 0 : (P.causal ? (min(N - 1, wq0 + 63) / kBK + 1) : P.n_kt);
     const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
+    const int n_diag = kt_end - kt_full;
+    // the diagonal (masked) tiles first, then the rest in order
+    auto tile_at = [&](int s) { return s < n_diag ? kt_full + s : s - n_diag; };
 
 #pragma unroll
     for (int j = 0; j < TPS; ++j)
-      if (j < kt_end) dt.issue(smem + j * DT::BYTES, j * kBK, w);
+      if (j < kt_end) dt.issue(smem + j * DT::BYTES, tile_at(j) * kBK, w);
 
-    TileMaxQueue<kSeg> tq(iq < N ? tilemax + ((size_t)bh * N + iq) * ktp : nullptr);
+    // lane l keeps query wq0 + l's maxima; lanes 0-31 and 32-63 form the
+    // wave's two query blocks
+    const int my_blk = (wq0 >> 5) + (lane >> 5);
+    BlkCodes bc(32 * my_blk < N ? blkc + ((size_t)bh * P.n_q32 + my_blk) * ktc : nullptr, lane, kt_full,
+                kt_end);
     float m = -INFINITY;
 
-    auto tile = [&](int kt, auto masked) {
-      const char* kl = smem + (kt % (2 * TPS)) * DT::BYTES;
+    auto tile = [&](int s, int kt, auto masked) -> float {
+      const char* kl = smem + (s % (2 * TPS)) * DT::BYTES;
       f32x4 acc[4][4];               // [query block][key block]
 #pragma unroll
       for (int b = 0; b < 4; ++b)
@@ -830,11 +864,11 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
       float pm[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        float t = __builtin_elementwise_maximum(acc[b][0][0], acc[b][0][1]);
+        float t = fmax_nan(acc[b][0][0], acc[b][0][1]);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int i = (kb == 0 ? 2 : 0); i < 4; ++i) t = __builtin_elementwise_maximum(t, acc[b][kb][i]);
+          for (int i = (kb == 0 ? 2 : 0); i < 4; ++i) t = fmax_nan(t, acc[b][kb][i]);
         pm[b] = t;
       }
       // Reduce over the four lane groups and scatter: group g keeps query
@@ -842,37 +876,41 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
       // (0,2) and (1,3); permlane16 swap then pairs (0,1) and (2,3).
       const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[0]), __float_as_uint(pm[2]), false, false);
       const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pm[1]), __float_as_uint(pm[3]), false, false);
-      const float a0 = __builtin_elementwise_maximum(__uint_as_float(s02[0]), __uint_as_float(s02[1]));
-      const float a1 = __builtin_elementwise_maximum(__uint_as_float(s13[0]), __uint_as_float(s13[1]));
+      const float a0 = fmax_nan(__uint_as_float(s02[0]), __uint_as_float(s02[1]));
+      const float a1 = fmax_nan(__uint_as_float(s13[0]), __uint_as_float(s13[1]));
       const auto s01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a0), __float_as_uint(a1), false, false);
-      const float tm = __builtin_elementwise_maximum(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
+      const float tm = fmax_nan(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
       m = fmaxf(m, tm);
-      tq.push(half_bits_up(tm * P.scale));
-      tq.tile_done(kt);
+      return half_max32(tm == -INFINITY ? -INFINITY : (tm - m) * P.scale);
     };
 
     // Step over TPS tiles: wait for them (issued one step earlier; this also
-    // retires the tile-max stores), bare barrier (a full __syncthreads would
-    // add a memory fence), issue the next step's tiles into the slots that
-    // the previous step read, compute.
-    for (int kt0 = 0; kt0 < kt_end; kt0 += TPS) {
+    // retires the code stores), bare barrier (a full __syncthreads would add a
+    // memory fence), issue the next step's tiles into the slots that the
+    // previous step read, compute.
+    for (int s0 = 0; s0 < kt_end; s0 += TPS) {
       wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int j = 0; j < TPS; ++j) {
-        const int kn = kt0 + TPS + j;
-        if (kn < kt_end) dt.issue(smem + (kn % (2 * TPS)) * DT::BYTES, kn * kBK, w);
+        const int sn = s0 + TPS + j;
+        if (sn < kt_end) dt.issue(smem + (sn % (2 * TPS)) * DT::BYTES, tile_at(sn) * kBK, w);
       }
 #pragma unroll
       for (int j = 0; j < TPS; ++j) {
-        const int kt = kt0 + j;
-        if (kt < kt_full)
-          tile(kt, std::false_type{});
-        else if (kt < kt_end_w)
-          tile(kt, std::true_type{});
+        const int s = s0 + j;
+        if (s >= kt_end) break;
+        const int kt = tile_at(s);
+        if (kt >= kt_full) {
+          const float r = kt < kt_end_w ? tile(s, kt, std::true_type{}) : -INFINITY;
+          bc.put_diag(kt, r);
+        } else {
+          bc.put(kt, tile(s, kt, std::false_type{}), kt_full);
+        }
       }
     }
-    tq.finish(max(kt_end_w, kt_full));
+    bc.finish(kt_full);
+    const int iq = wq0 + lane;
     if (iq < N) rowmax[(size_t)bh * N + iq] = m * P.scale;
   };
 
@@ -974,13 +1012,183 @@ __device__ __forceinline__ float model_pow(float z, float beta, float& deriv) {
   }
 }
 
+// ------------------------------------------------- histogram start ---
+// A row's histogram over the bracket [lo, hi]: BINS uniform bins of
+// y = x - lo, per bin two 64-bit words of integer moments in units of
+// 2^-hshift (count << 40 plus sum Y, and sum Y^2; see hist_add).  From it:
+// tau's bin, a start value inside it and, for alpha in {1.5, 2} (where f is
+// exact at the bin edges), the bracket narrowed to that bin.  The pages give
+// only "a coarse histogram kept on chip" ("AdaSplash-2: The Transformer
+// Revolution We Didn't See Coming", "Sparse Attention Makes Waves"); the bin
+// count, the moments and the two-point start model are this library's.
+__device__ __forceinline__ void hist_add(unsigned long long* hr, float y, float bin_scale, float ysc,
+                                         unsigned ymax, int bins) {
+  if (y > 0.0f) {
+    const unsigned Y = min((unsigned)(fminf(y, 1.0f) * ysc), ymax);
+    const int b = min((int)(y * bin_scale), bins - 1);
+    atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
+    atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
+  }
+}
+
+template <int AK, int BINS>
+__device__ __forceinline__ void hist_start(const unsigned long long* hr, float width, float xmax, int hshift,
+                                        float beta, float& lo, float& hi, float& tau) {
+  const double yunit = ldexp(1.0, -hshift), yunit2 = yunit * yunit;   // fixed-point units
+  const double bw = (double)width / BINS;     // bin width in y = x - lo
+  const bool exact = (AK == AK15 || AK == AK20);
+  double C = 0, S1 = 0, S2 = 0;       // moments of the bins above the edge under test
+  double f_hi = -1.0;                  // f at the upper edge of the bin under test
+  int bstar = 0;
+  double f_lo = 0, cstar = 0, Cs = 0, S1s = 0, S2s = 0;
+  // Other alpha (estimate only): the elements of every bin b0.. stand
+  // half at mu - sd and half at mu + sd of their bin, which keeps the
+  // bin's count, sum and sum of squares.  Returns f of that model at t
+  // (float: a start value needs no more) and its derivative in df.
+  auto model_f = [&](int b0, float t, float& df) -> float {
+    float fv = -1.0f;
+    df = 0.0f;
+    for (int bb = b0; bb < BINS; ++bb) {
+      const unsigned long long g1 = hr[2 * bb], g2 = hr[2 * bb + 1];
+      const float cc = (float)(g1 >> 40);
+      if (cc > 0.0f) {
+        const float mu = (float)((double)(g1 & ((1ull << 40) - 1ull)) * yunit) / cc;
+        const float sd = sqrtf(fmaxf((float)((double)g2 * yunit2) / cc - mu * mu, 0.0f));
+        float da, db;
+        const float va = model_pow<AK>(mu + sd - t, beta, da);
+        const float vb = model_pow<AK>(mu - sd - t, beta, db);
+        fv += 0.5f * cc * (va + vb);
+        df -= 0.5f * cc * beta * (da + db);
+      }
+    }
+    return fv;
+  };
+  for (int b = exact ? BINS - 1 : -1; b >= 0; --b) {   // the exact edge values
+    const unsigned long long h1 = hr[2 * b], h2 = hr[2 * b + 1];
+    const double cb = (double)(h1 >> 40);
+    const double s1 = (double)(h1 & ((1ull << 40) - 1ull)) * yunit;
+    const double s2 = (double)h2 * yunit2;
+    const double e = (double)b * bw;
+    const double Cn = C + cb, S1n = S1 + s1, S2n = S2 + s2;
+    double f;
+    if (AK == AK15) {
+      f = S2n - 2.0 * e * S1n + e * e * Cn - 1.0;      // exact at the edge
+    } else {
+      f = S1n - e * Cn - 1.0;                          // AK20: exact at the edge
+    }
+    if (f >= 0.0 || b == 0) {
+      bstar = b;
+      f_lo = f;
+      cstar = cb;
+      Cs = C;
+      S1s = S1;
+      S2s = S2;
+      break;
+    }
+    f_hi = f;
+    C = Cn;
+    S1 = S1n;
+    S2 = S2n;
+  }
+  if (!exact) {
+    // the model decreases in t: tau's bin by bisection over the edges
+    int blo = 0, bhi = BINS;
+    while (bhi - blo > 1) {
+      const int mid = (blo + bhi) >> 1;
+      float df;
+      if (model_f(mid, (float)(mid * bw), df) >= 0.0f) blo = mid; else bhi = mid;
+    }
+    bstar = blo;
+  }
+  const double eb = (double)bstar * bw, eb1 = (double)(bstar + 1) * bw;
+  double t0 = -1.0;
+  if (!exact) {
+    // Newton on the model from the bin's lower edge: the model is convex
+    // and decreasing, so the steps rise monotonically to its root
+    float t = (float)eb;
+    const float tmax = (float)eb1, dt = 1e-6f * (float)bw;
+    for (int it2 = 0; it2 < 8; ++it2) {
+      float df;
+      const float fv = model_f(bstar, t, df);
+      if (!(fv > 0.0f) || !(df < 0.0f)) break;
+      const float tn = fminf(t - fv / df, tmax);
+      if (!(tn > t + dt)) {
+        t = fmaxf(t, tn);
+        break;
+      }
+      t = tn;
+    }
+    t0 = (double)t;
+  }
+  if (exact && cstar == 0.0 && Cs > 0.0) {
+    // the tau bin is empty: the support is exactly the bins above it
+    if (AK == AK15) {
+      const double disc = S1s * S1s - Cs * (S2s - 1.0);
+      if (disc >= 0.0) t0 = (S1s - sqrt(disc)) / Cs;
+    } else {
+      t0 = (S1s - 1.0) / Cs;
+    }
+    if (!(t0 >= eb && t0 <= eb1)) t0 = -1.0;
+  }
+  if (exact && t0 < 0.0 && cstar > 0.0) {
+    // tau's bin holds elements: f is exact for the bins above it, and the
+    // bin's own cstar elements are replaced by cstar/2 at each of mu - sd
+    // and mu + sd, which keeps their count, sum and sum of squares.  The
+    // model equals f at both edges; its root is the start.
+    const unsigned long long g1 = hr[2 * bstar], g2 = hr[2 * bstar + 1];
+    const double s1b = (double)(g1 & ((1ull << 40) - 1ull)) * yunit;
+    const double s2b = (double)g2 * yunit2;
+    const double mu = s1b / cstar;
+    const double sd = sqrt(fmax(s2b / cstar - mu * mu, 0.0));
+    const double p2 = mu + sd;
+    const double q1 = fmin(fmax(mu - sd, eb), eb1), q2 = fmin(fmax(p2, eb), eb1);
+    // segments [eb, q1], [q1, q2], [q2, eb1]: moments of what lies above tau
+    const double segA[3] = {Cs + cstar, Cs + 0.5 * cstar, Cs};
+    const double segB[3] = {S1s + s1b, S1s + 0.5 * cstar * p2, S1s};
+    const double segS[3] = {S2s + s2b, S2s + 0.5 * cstar * p2 * p2, S2s};
+    const double segR[3] = {q1, q2, eb1};
+    double a0 = eb;
+    for (int sg = 0; sg < 3; ++sg) {
+      const double A = segA[sg], B = segB[sg], S = segS[sg], a1 = segR[sg];
+      const double fr = (AK == AK15) ? S - 2.0 * a1 * B + a1 * a1 * A - 1.0 : B - a1 * A - 1.0;
+      if (a1 > a0 && fr <= 0.0) {
+        double t = -1.0;
+        if (AK == AK15) {
+          const double disc = B * B - A * (S - 1.0);
+          if (A > 0.0 && disc >= 0.0) t = (B - sqrt(disc)) / A;
+        } else if (A > 0.0) {
+          t = (B - 1.0) / A;
+        }
+        if (t >= 0.0) t0 = fmin(fmax(t, a0), a1);
+        break;
+      }
+      a0 = fmax(a0, a1);
+    }
+  }
+  if (t0 < 0.0) {
+    const double den = f_lo - f_hi;
+    t0 = den > 0.0 ? eb + (eb1 - eb) * (f_lo / den) : 0.5 * (eb + eb1);
+  }
+  const float t0x = (float)((double)lo + t0);
+  if (exact) {
+    // float rounding of x and lo, and the fixed-point truncation of y
+    const float margin = fmaxf(1.0f, fabsf(xmax)) * 5e-7f + 1e-6f + (float)(2.0 * yunit);
+    const float nlo = (float)((double)lo + eb) - margin;
+    const float nhi = (float)((double)lo + eb1) + margin;
+    if (nlo > lo) lo = nlo;
+    if (nhi < hi) hi = nhi;
+  }
+  tau = fminf(fmaxf(t0x, lo), hi);
+}
+
 // ------------------------------------------------------------- k_tau ---
-// Per workgroup (128 queries, 32 per wave): bracket from the row maxima and
-// the row's tile maxima, candidate key tiles, histogram initialisation,
-// Halley / bisection sweeps over candidate tiles, tau, iteration counts and
-// the block mask.  Dynamic LDS: K double buffer | histogram [128][BINS*2+2] u64 |
+// Per workgroup (128 queries, 32 per wave): bracket from the row maxima,
+// candidate key tiles from the block codes, histogram initialisation, Halley /
+// bisection sweeps over candidate tiles, tau, iteration counts and the block
+// mask.  Dynamic LDS: K double buffer | histogram [128][BINS*2+2] u64 |
 // list i16[kChunk] | wave bits u8[kChunk] | flags u8[kChunk] |
-// candidate bits u32[4][n_words] | counter.
+// candidate bits u32[4][n_words] | counter | final mask bits u32[4][n_words] |
+// bits of tiles above the lower bracket end u32[4][n_words].
 constexpr int kChunk = 512;    // key tiles listed at once
 
 template <typename E, int D>
@@ -996,7 +1204,7 @@ template <typename E, int D, int AK, int BINS>
 __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
                                                   const E* __restrict__ V,
                                                   const float* __restrict__ rowmax,
-                                                  const uint16_t* __restrict__ tilemax, Params P,
+                                                  const uint8_t* __restrict__ blkc, Params P,
                                                   float* __restrict__ tau_out,
                                                   uint8_t* __restrict__ mask_out,
                                                   uint8_t* __restrict__ iters_out,
@@ -1030,30 +1238,16 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   uint32_t* cbits = reinterpret_cast<uint32_t*>(flags + kChunk);      // [4][n_words]
   int* counter = reinterpret_cast<int*>(cbits + kWaves * n_words);
   uint32_t* mbits = reinterpret_cast<uint32_t*>(counter + 16);        // [4][n_words] final mask
+  uint32_t* lbits = mbits + kWaves * n_words;                         // [4][n_words] tiles above lo
 
   const int wq_last = min(N - 1, wq0 + kBQ - 1);
   const int kt_end_w = !wave_rows ? 0 : (P.causal ? wq_last / kBK + 1 : P.n_kt);
   const int kt_end = P.causal ? (min(N - 1, q0 + kBQW - 1) / kBK + 1) : P.n_kt;
   const bool wave_has_tail = wq0 + kBQ > N;
-
-  const int ktp = tilemax_row(P.n_kt);
-  // this row's tile maxima; lane half h reads the groups of 8 tiles 2i + h
-  const uint16_t* tmx = tilemax + ((size_t)bh * N + (valid ? iq : 0)) * ktp;
-  // 2 kGB groups of 8 tiles (kGB per lane half) per batch
-  constexpr int kGB = AK == AKGEN ? 4 : 8;
-  auto load_groups = [&](int g0, u32x4 (&r)[kGB]) {
-#pragma unroll
-    for (int u = 0; u < kGB; ++u) {
-      const int g = g0 + 2 * u + h;
-      if (valid && g * 8 < kt_end_w)
-        r[u] = *reinterpret_cast<const u32x4*>(tmx + g * 8);
-      else
-        r[u] = u32x4{0xFC00FC00u, 0xFC00FC00u, 0xFC00FC00u, 0xFC00FC00u};
-    }
-  };
-  // the first batch is in flight together with the query fragments
-  u32x4 pre[kGB];
-  load_groups(0, pre);
+  // this wave's block codes; one 16-byte chunk per lane covers 1024 tiles
+  const uint8_t* crow = blkc + ((size_t)bh * P.n_q32 + (size_t)min(r32, P.n_q32 - 1)) * blk_row(P.n_kt);
+  u32x4 pre = u32x4{~0u, ~0u, ~0u, ~0u};
+  if (16 * lane < kt_end_w) pre = *reinterpret_cast<const u32x4*>(crow + 16 * lane);
 
   Frag<E> qf[D / 16];
   load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
@@ -1074,122 +1268,58 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   bool conv = !valid;
   int iters = 0;
   const double beta = (double)P.beta;
-  int* ncand = counter + 1;                                   // [4]
-  // half bits of tile g*8 + j from a loaded group (-inf past the wave's end)
-  auto group_half = [&](const u32x4& r, int g, int j) -> uint16_t {
-    const uint32_t wrd = r[j >> 1];
-    const uint16_t b = (uint16_t)((j & 1) ? (wrd >> 16) : (wrd & 0xFFFFu));
-    return (g * 8 + j < kt_end_w) ? b : (uint16_t)0xFC00u;
-  };
 
-  // ---- candidate key tiles: bit kt of wave w is set when some row of the
-  // wave has a tile maximum above its lower bracket end (tau >= lo, so no
-  // other tile can hold a nonzero probability for the wave).  Returns the
-  // workgroup's number of candidate wave-tiles, counted as if skipping were
-  // on, so that every decision taken from it is the same either way.
-  auto make_cand = [&](auto use_pre) -> int {
-    __syncthreads();   // earlier readers of the bits and counts are done
-    const float lim = valid ? lo - 4.0f * FLT_EPSILON * fmaxf(1.0f, fabsf(lo)) : INFINITY;
-    int total = 0;
-    // batch of 16 kGB tiles = kGB / 2 words; group g = 2i + h covers tiles 8g..8g+7
-    for (int g0 = 0; g0 * 8 < kt_end; g0 += 2 * kGB) {   // later tiles are never listed
-      u32x4 r[kGB];
-      if (decltype(use_pre)::value && g0 == 0) {
+  // ---- candidate key tiles: bit kt of wave w is set when the block code of
+  // tile kt admits a score above some row's lower bracket end (tau >= lo, so
+  // no other tile can hold a nonzero probability for the wave).  The test
+  // compares the code with the smallest lo_i - max_j x_ij of the wave's rows,
+  // less a margin for the float rounding of both sides.  Words past the
+  // wave's last visible tile are written as zeros up to the workgroup's end.
+  auto make_cand = [&](auto use_pre) {
+    __syncthreads();   // earlier readers of the bits are done
+    // (the MFMA shapes of the row-max sweep and of this kernel round their
+    // partial sums differently: 64 float epsilons of |x| covers that)
+    float th = valid ? (lo - xmax) - 64.0f * FLT_EPSILON * (fmaxf(1.0f, fabsf(xmax)) + 2.0f) : INFINITY;
+    th = half_min32(th);           // both lane halves hold the same 32 rows
+    const float lim = -128.0f * th;   // candidate iff code < lim
+    for (int base = 0; base < kt_end; base += 64 * 16) {
+      const int t0 = base + 16 * lane;
+      u32x4 r = u32x4{~0u, ~0u, ~0u, ~0u};
+      if (decltype(use_pre)::value && base == 0)
+        r = pre;
+      else if (t0 < kt_end_w)
+        r = *reinterpret_cast<const u32x4*>(crow + t0);
+      uint32_t bits = 0;
 #pragma unroll
-        for (int u = 0; u < kGB; ++u) r[u] = pre[u];
-      } else {
-        load_groups(g0, r);
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t c = (r[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+        if ((float)c < lim && t0 + j < kt_end_w) bits |= 1u << j;
       }
-      // this row's candidate bits, 8 per group, then OR over the half's rows
-      uint32_t pl[kGB / 4];
-#pragma unroll
-      for (int q = 0; q < kGB / 4; ++q) pl[q] = 0u;
-#pragma unroll
-      for (int u = 0; u < kGB; ++u)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (half_up_value(group_half(r[u], g0 + 2 * u + h, j)) > lim) pl[u >> 2] |= 1u << (8 * (u & 3) + j);
-#pragma unroll
-      for (int q = 0; q < kGB / 4; ++q) {
-        const unsigned long long hv = half_or_dpp(pl[q]);
-        const uint32_t h0 = (uint32_t)hv, h1 = (uint32_t)(hv >> 32);
-        // word k of this batch: groups g0+4k (half 0, u=2k), g0+4k+1 (half 1,
-        // u=2k), g0+4k+2 (half 0, u=2k+1), g0+4k+3 (half 1, u=2k+1)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int sh = 16 * kk;
-          const uint32_t real = ((h0 >> sh) & 0xFFu) | (((h1 >> sh) & 0xFFu) << 8) |
-                                (((h0 >> (sh + 8)) & 0xFFu) << 16) | (((h1 >> (sh + 8)) & 0xFFu) << 24);
-          const int wd = (g0 * 8 >> 5) + 2 * q + kk;
-          const int nv = min(max(kt_end_w - 32 * wd, 0), 32);
-          const uint32_t vis = nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u);
-          total += __popc(real);
-          if (lane == 0 && wd < n_words) cbits[w * n_words + wd] = dense ? vis : real;
-        }
-      }
+      const int nv = min(max(kt_end_w - t0, 0), 16);
+      if (dense) bits = nv >= 16 ? 0xFFFFu : ((1u << nv) - 1u);
+      // lanes 2m and 2m+1 hold the two halves of word (base / 32) + m
+      const uint32_t word = bits | (dpp_u<0xB1>(bits) << 16);
+      const int wd = (base >> 5) + (lane >> 1);
+      if (!(lane & 1) && wd < n_words) cbits[w * n_words + wd] = word;
     }
-    if (lane == 0) ncand[w] = total;
     __syncthreads();
-    return ncand[0] + ncand[1] + ncand[2] + ncand[3];
   };
   auto cand = [&](int ww, int kt) -> bool { return (cbits[ww * n_words + (kt >> 5)] >> (kt & 31)) & 1u; };
-  // visible wave-tiles of the workgroup (the same for every thread)
-  int vis_total = 0;
-  for (int ww = 0; ww < kWaves; ++ww) {
-    const int wq = q0 + kBQ * ww;
-    if (wq < N) vis_total += P.causal ? min(N - 1, wq + kBQ - 1) / kBK + 1 : P.n_kt;
-  }
-  // Pruning pays for its extra passes over the tile maxima (a few memory
-  // round trips) only when the bracket [max x - 1, ...] leaves many tiles
-  // standing, both in number and as a share of the visible ones.
-  const int n_cand0 = make_cand(std::true_type{});
-  const bool wide = n_cand0 >= 64 && n_cand0 * 8 > vis_total;
-
-  // ---- lower bracket end from the row's tile maxima M_t.  Every tile holds
-  // its maximum element, so g(t) = sum_t [M_t - t]_+^beta - 1 <= f(t): g's root
-  // is a valid lower bound on tau, and a tight one when many tiles reach near
-  // the row maximum.  Halley-bisection on g over lower bounds of the tile
-  // maxima (the two lane halves take alternate tiles); the largest point with
-  // g >= 0 is kept.
-  if (wide && P.mode != EA_TAU_BISECT) {
-    float glo = lo, ghi = hi, tg = lo;
-    for (int it = 0; it < 3; ++it) {
-      float G0 = 0, G1 = 0, G2 = 0, gc = 0;
-      for (int g0 = 0; g0 * 8 < kt_end_w; g0 += 2 * kGB) {
-        u32x4 r[kGB];
-        load_groups(g0, r);
-#pragma unroll
-        for (int u = 0; u < kGB; ++u)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            Ent<AK>::sweep(clamp01(half_down_value(group_half(r[u], g0 + 2 * u + h, j)) - tg), P.beta,
-                           G0, G1, G2, gc);
-      }
-      G0 += __shfl_xor(G0, 32);
-      G1 += __shfl_xor(G1, 32);
-      G2 += __shfl_xor(G2, 32);
-      const double g = (double)G0 - 1.0;
-      if (g >= 0.0) glo = tg; else ghi = tg;
-      const double ulp = (double)FLT_EPSILON * fmax(1.0, fabs((double)tg));
-      const double gp = -beta * (double)G1;
-      const double gpp = (AK == AK20) ? 0.0 : beta * (beta - 1.0) * (double)G2;
-      const double th = (double)tg - 2.0 * g * gp / (2.0 * gp * gp - g * gpp);
-      float nt = (th > (double)glo && th < (double)ghi) ? (float)th : glo + 0.5f * (ghi - glo);
-      if (!(nt > glo && nt < ghi) || fabs(g) <= 2.0 * fabs(gp) * ulp || ghi - glo <= 4.0f * (float)ulp) break;
-      tg = nt;
-    }
-    glo -= 4.0f * FLT_EPSILON * fmaxf(1.0f, fabsf(glo));
-    if (valid && glo > lo) lo = fminf(glo, hi);
-    make_cand(std::false_type{});
-  }
+  make_cand(std::true_type{});
 
   // ---- histogram initialisation (AdaSplash-2)
   if (P.mode == EA_TAU_HIST_HALLEY) {
     for (int e = threadIdx.x; e < kBQW * HROW; e += kThreads) hist[e] = 0ull;
     unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * HROW;
-    // bins split [lo, hi]; moments are kept in units of 2^-24 of y = x - lo <= 1
+    // Bins split [lo, hi]; moments are kept in units of 2^-S of y = x - lo <= 1
+    // with Y <= 2^S - 1: the count sits at bit 40, sum Y below it and sum Y^2
+    // in a word of its own, so with at most N <= 2^(40-S) elements per bin
+    // sum Y < 2^40 and sum Y^2 < 2^64.  S = 24 up to N = 65536, fewer bits
+    // beyond (the host chooses S from N).
     const float width = valid ? fmaxf(hi - lo, 1e-30f) : 1.0f;
     const float bin_scale = (float)BINS / width;
+    const float ysc = (float)(1u << P.hshift);
+    const unsigned ymax = (1u << P.hshift) - 1u;
     for (int base = 0; base < kt_end; base += kChunk) {
       const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
       RowTiles<E, D, kBK> st(Kh, N, w, lane);
@@ -1210,13 +1340,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int j = 0; j < 16; ++j) {
-                const float y = fmaf(acc[kb][j], P.scale, -lo);
-                if (y > 0.0f) {
-                  const unsigned Y = (unsigned)(fminf(y, 1.0f) * 16777216.0f);
-                  const int b = min((int)(y * bin_scale), BINS - 1);
-                  atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
-                  atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
-                }
+                hist_add(hr, fmaf(acc[kb][j], P.scale, -lo), bin_scale, ysc, ymax, BINS);
               }
           };
           if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
@@ -1228,154 +1352,9 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         __syncthreads();
       }
     }
-    if (valid) {
-      const double inv24 = 1.0 / 16777216.0, inv48 = inv24 * inv24;
-      const double bw = (double)width / BINS;     // bin width in y = x - lo
-      const bool exact = (AK == AK15 || AK == AK20);
-      double C = 0, S1 = 0, S2 = 0;       // moments of the bins above the edge under test
-      double f_hi = -1.0;                  // f at the upper edge of the bin under test
-      int bstar = 0;
-      double f_lo = 0, cstar = 0, Cs = 0, S1s = 0, S2s = 0;
-      // Other alpha (estimate only): the elements of every bin b0.. stand
-      // half at mu - sd and half at mu + sd of their bin, which keeps the
-      // bin's count, sum and sum of squares.  Returns f of that model at t
-      // (float: a start value needs no more) and its derivative in df.
-      auto model_f = [&](int b0, float t, float& df) -> float {
-        float fv = -1.0f;
-        df = 0.0f;
-        for (int bb = b0; bb < BINS; ++bb) {
-          const unsigned long long g1 = hr[2 * bb], g2 = hr[2 * bb + 1];
-          const float cc = (float)(g1 >> 40);
-          if (cc > 0.0f) {
-            const float mu = (float)((double)(g1 & ((1ull << 40) - 1ull)) * inv24) / cc;
-            const float sd = sqrtf(fmaxf((float)((double)g2 * inv48) / cc - mu * mu, 0.0f));
-            float da, db;
-            const float va = model_pow<AK>(mu + sd - t, P.beta, da);
-            const float vb = model_pow<AK>(mu - sd - t, P.beta, db);
-            fv += 0.5f * cc * (va + vb);
-            df -= 0.5f * cc * P.beta * (da + db);
-          }
-        }
-        return fv;
-      };
-      for (int b = exact ? BINS - 1 : -1; b >= 0; --b) {   // the exact edge values
-        const unsigned long long h1 = hr[2 * b], h2 = hr[2 * b + 1];
-        const double cb = (double)(h1 >> 40);
-        const double s1 = (double)(h1 & ((1ull << 40) - 1ull)) * inv24;
-        const double s2 = (double)h2 * inv48;
-        const double e = (double)b * bw;
-        const double Cn = C + cb, S1n = S1 + s1, S2n = S2 + s2;
-        double f;
-        if (AK == AK15) {
-          f = S2n - 2.0 * e * S1n + e * e * Cn - 1.0;      // exact at the edge
-        } else {
-          f = S1n - e * Cn - 1.0;                          // AK20: exact at the edge
-        }
-        if (f >= 0.0 || b == 0) {
-          bstar = b;
-          f_lo = f;
-          cstar = cb;
-          Cs = C;
-          S1s = S1;
-          S2s = S2;
-          break;
-        }
-        f_hi = f;
-        C = Cn;
-        S1 = S1n;
-        S2 = S2n;
-      }
-      if (!exact) {
-        // the model decreases in t: tau's bin by bisection over the edges
-        int blo = 0, bhi = BINS;
-        while (bhi - blo > 1) {
-          const int mid = (blo + bhi) >> 1;
-          float df;
-          if (model_f(mid, (float)(mid * bw), df) >= 0.0f) blo = mid; else bhi = mid;
-        }
-        bstar = blo;
-      }
-      const double eb = (double)bstar * bw, eb1 = (double)(bstar + 1) * bw;
-      double t0 = -1.0;
-      if (!exact) {
-        // Newton on the model from the bin's lower edge: the model is convex
-        // and decreasing, so the steps rise monotonically to its root
-        float t = (float)eb;
-        const float tmax = (float)eb1, dt = 1e-6f * (float)bw;
-        for (int it2 = 0; it2 < 8; ++it2) {
-          float df;
-          const float fv = model_f(bstar, t, df);
-          if (!(fv > 0.0f) || !(df < 0.0f)) break;
-          const float tn = fminf(t - fv / df, tmax);
-          if (!(tn > t + dt)) {
-            t = fmaxf(t, tn);
-            break;
-          }
-          t = tn;
-        }
-        t0 = (double)t;
-      }
-      if (exact && cstar == 0.0 && Cs > 0.0) {
-        // the tau bin is empty: the support is exactly the bins above it
-        if (AK == AK15) {
-          const double disc = S1s * S1s - Cs * (S2s - 1.0);
-          if (disc >= 0.0) t0 = (S1s - sqrt(disc)) / Cs;
-        } else {
-          t0 = (S1s - 1.0) / Cs;
-        }
-        if (!(t0 >= eb && t0 <= eb1)) t0 = -1.0;
-      }
-      if (exact && t0 < 0.0 && cstar > 0.0) {
-        // tau's bin holds elements: f is exact for the bins above it, and the
-        // bin's own cstar elements are replaced by cstar/2 at each of mu - sd
-        // and mu + sd, which keeps their count, sum and sum of squares.  The
-        // model equals f at both edges; its root is the start.
-        const unsigned long long g1 = hr[2 * bstar], g2 = hr[2 * bstar + 1];
-        const double s1b = (double)(g1 & ((1ull << 40) - 1ull)) * inv24;
-        const double s2b = (double)g2 * inv48;
-        const double mu = s1b / cstar;
-        const double sd = sqrt(fmax(s2b / cstar - mu * mu, 0.0));
-        const double p2 = mu + sd;
-        const double q1 = fmin(fmax(mu - sd, eb), eb1), q2 = fmin(fmax(p2, eb), eb1);
-        // segments [eb, q1], [q1, q2], [q2, eb1]: moments of what lies above tau
-        const double segA[3] = {Cs + cstar, Cs + 0.5 * cstar, Cs};
-        const double segB[3] = {S1s + s1b, S1s + 0.5 * cstar * p2, S1s};
-        const double segS[3] = {S2s + s2b, S2s + 0.5 * cstar * p2 * p2, S2s};
-        const double segR[3] = {q1, q2, eb1};
-        double a0 = eb;
-        for (int sg = 0; sg < 3; ++sg) {
-          const double A = segA[sg], B = segB[sg], S = segS[sg], a1 = segR[sg];
-          const double fr = (AK == AK15) ? S - 2.0 * a1 * B + a1 * a1 * A - 1.0 : B - a1 * A - 1.0;
-          if (a1 > a0 && fr <= 0.0) {
-            double t = -1.0;
-            if (AK == AK15) {
-              const double disc = B * B - A * (S - 1.0);
-              if (A > 0.0 && disc >= 0.0) t = (B - sqrt(disc)) / A;
-            } else if (A > 0.0) {
-              t = (B - 1.0) / A;
-            }
-            if (t >= 0.0) t0 = fmin(fmax(t, a0), a1);
-            break;
-          }
-          a0 = fmax(a0, a1);
-        }
-      }
-      if (t0 < 0.0) {
-        const double den = f_lo - f_hi;
-        t0 = den > 0.0 ? eb + (eb1 - eb) * (f_lo / den) : 0.5 * (eb + eb1);
-      }
-      const float t0x = (float)((double)lo + t0);
-      if (exact) {
-        const float margin = fmaxf(1.0f, fabsf(xmax)) * 5e-7f + 1e-6f;
-        const float nlo = (float)((double)lo + eb) - margin;
-        const float nhi = (float)((double)lo + eb1) + margin;
-        if (nlo > lo) lo = nlo;
-        if (nhi < hi) hi = nhi;
-      }
-      tau = fminf(fmaxf(t0x, lo), hi);
-    }
+    if (valid) hist_start<AK, BINS>(hr, width, xmax, P.hshift, P.beta, lo, hi, tau);
     // the histogram narrowed lo to tau's bin: prune the candidates again
-    if (wide && (AK == AK15 || AK == AK20)) make_cand(std::false_type{});
+    if (AK == AK15 || AK == AK20) make_cand(std::false_type{});
   } else if (P.mode == EA_TAU_HALLEY_BISECT) {
     tau = lo;
   } else {
@@ -1395,7 +1374,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     }
   }
   const int max_iters = P.max_iters;
-  // The candidate tiles do not change between refinement sweeps.  When the
+  // The candidate tiles only shrink between refinement sweeps.  When the
   // workgroup's fit beside the K double buffer in the histogram's space (dead
   // from here), they are copied once and every sweep reads them in place: no
   // list rebuild, copy or barrier per tile.
@@ -1419,9 +1398,12 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   for (int sweep = 0; sweep <= max_iters + 1; ++sweep) {
     const bool wave_busy = __ballot(!conv) != 0ull;
     if (!__syncthreads_or(wave_busy ? 1 : 0)) break;
-    if (kFusePV && wave_busy && !dense) {
-      // this sweep rewrites the wave's mask
-      for (int e = lane; e < n_words; e += kWave) mbits[w * n_words + e] = 0u;
+    if (wave_busy && !dense) {
+      // this sweep rewrites the wave's mask and its tiles above lo
+      for (int e = lane; e < n_words; e += kWave) {
+        if (kFusePV) mbits[w * n_words + e] = 0u;
+        lbits[w * n_words + e] = 0u;
+      }
     }
     float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
     // f, f', f'' terms of key tile kt (staged at kl) and its mask bits
@@ -1441,6 +1423,13 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
           const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
           if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
           if (kFusePV && any && lane == 0) atomicOr(&mbits[w * n_words + (kt >> 5)], 1u << (kt & 31));
+          // does the tile hold a score above some row's lower bracket end?
+          float mx = fmax_nan(acc[0][0], acc[1][0]);
+#pragma unroll
+          for (int j = 1; j < 16; ++j) mx = fmax_nan(mx, fmax_nan(acc[0][j], acc[1][j]));
+          // (the ballot runs on every lane: it must see every row)
+          const bool above = __ballot(fmaf(mx, P.scale, -lo) > 0.0f) != 0ull;
+          if (above && lane == 0) atomicOr(&lbits[w * n_words + (kt >> 5)], 1u << (kt & 31));
         }
       };
       if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
@@ -1450,7 +1439,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     };
     if (n_res >= 0) {
       for (int i = 0; i < n_res; ++i)
-        if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(list[i], slot(i));
+        if (wave_busy && cand(w, list[i])) sweep_tile(list[i], slot(i));
     } else {
       for (int base = 0; base < kt_end; base += kChunk) {
         const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
@@ -1489,9 +1478,14 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         } else {
           double next = 0.5 * ((double)lo + (double)hi);
           if (!bisect) {
+            // Halley while |f f''| < f'^2; there the step lies between 2/3 and
+            // 2 Newton steps, so a step of two ulps means |f| within three ulps
+            // of |f'|.  Otherwise (for 1.5 < alpha < 2, f'' grows without bound
+            // as a score nears tau from above) a Newton step.
             const double fpp = (AK == AK20) ? 0.0 : beta * (beta - 1.0) * (double)F2;
-            const double den = 2.0 * fp * fp - f * fpp;
-            const double th = (double)tau - 2.0 * f * fp / den;
+            const bool halley = fabs(f * fpp) < fp * fp;
+            const double th = halley ? (double)tau - 2.0 * f * fp / (2.0 * fp * fp - f * fpp)
+                                     : (double)tau - f / fp;
             if (fabs(th - (double)tau) <= 2.0 * ulp) {
               conv = true;                        // converged: keep the evaluated tau
             } else if (th > (double)lo && th < (double)hi) {
@@ -1506,6 +1500,14 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
           }
         }
       }
+    }
+    // Candidates of the next sweep: tau only moves up from lo, so a tile with
+    // no score above the lo this sweep used stays empty for every row; a wave
+    // whose rows have all converged needs none.  (Only this wave's bits are
+    // written; every reader of them passed a barrier since its last read.)
+    if (wave_busy && !dense) {
+      const bool busy_next = __ballot(!conv) != 0ull;
+      for (int e = lane; e < n_words; e += kWave) cbits[w * n_words + e] = busy_next ? lbits[w * n_words + e] : 0u;
     }
   }
 
@@ -2048,6 +2050,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         const float* dels = taus + kBQ;
         // S = Q K^T and dP = dO V^T: rows = the 32 queries, column = this lane's key
         f32x16 sacc = f32x16{}, pacc = f32x16{};
+        [[maybe_unused]] double sd[kTr ? 1 : 16] = {};
 #pragma unroll
         for (int c = 0; c < D / 16; ++c) {
           Frag<E> a, b;
@@ -2056,12 +2059,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
             Frag<E> kc;
             ld8(kc, reinterpret_cast<const E*>(klds + (32 * w + c32) * KS) + 16 * c + 8 * h);
             mma(sacc, a, kc);
+          } else if constexpr (!kTr) {
+            mma_chunk64(sd, a, kf[c]);
           } else {
             mma(sacc, a, kf[c]);
           }
           ld8(b, reinterpret_cast<const E*>(otl + c32 * KS) + 16 * c + 8 * h);
           mma(pacc, b, vf[c]);
         }
+        if constexpr (!kTr) round_acc(sacc, sd);
         // query rows r (acc_row) are visible to this lane's key when
         // jk - qb0 <= r <= N - 1 - qb0 (causal) and the key exists
         auto softmax_like = [&](auto masked) {
@@ -2088,9 +2094,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
           softmax_like(std::false_type{});
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          Frag<E> pf, sf;
+          // dK = sum_i dS_ij q_i: the queries of a cluster are nearly parallel
+          // and large, so the bf16 rounding of dS alone would cost about the
+          // whole stated tolerance on some keys' rows; dS goes in as a hi/lo
+          // bf16 pair, as in the dQ kernel.
+          Frag<E> pf, sf, sl;
           from_acc(pf, sacc, 8 * s);
-          from_acc(sf, pacc, 8 * s);
+          split_acc(sf, sl, pacc, 8 * s);
           const int qoff = 16 * s + 4 * h;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) {
@@ -2106,6 +2116,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
             }
             mma(dva[db], pf, ob);
             mma(dka[db], sf, qb);
+            if constexpr (kNeedsLo<E>) mma(dka[db], sl, qb);
           }
         }
       }
@@ -2133,6 +2144,202 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         reinterpret_cast<float*>(dk)[off] = kk;
       }
     }
+}
+
+// ------------------------------------------------------- k_entmax_rows ---
+// alpha-entmax of materialised score rows (no attention): x = (alpha-1) s,
+// tau per row, p = [x - tau]_+^(1/(alpha-1)) ("AdaSplash: Adaptive Sparse
+// Flash Attention", "Accelerated Alpha-Entmax Transformation": the transform
+// on its own, where Halley-bisection replaces plain bisection).  One wave per
+// row: lane l holds elements 4 (l + 64 c) .. +3 for chunks c, in registers
+// when the row has at most 64 T elements (T > 0), else read again from memory
+// by every sweep (T = 0).  Sweep sums are reduced across the wave with DPP and
+// lane permutes, so no barrier is involved; the histogram is the wave's own
+// in LDS.  -inf scores are masked entries (p = 0, not counted in n).
+struct RowParams {
+  long long rows;
+  int n, mode, max_iters, hshift, vec;
+  float scale, beta, alpha, tol;
+};
+constexpr int kRowBins = 16;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) { return v + dpp_f<CTRL>(v); }
+// sum over the whole wave, the same on every lane (fixed order: deterministic)
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  v = dpp_add<0x141>(v);
+  v = dpp_add<0x140>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = half_max32(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmax_nan(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+template <typename E>
+__device__ __forceinline__ f32x4 load4(const E* row, int e, int n, bool vec) {
+  f32x4 r = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (vec && e + 3 < n) {
+    if constexpr (sizeof(E) == 4) {
+      r = *reinterpret_cast<const f32x4*>(row + e);
+    } else {
+      const bf16x4 b = *reinterpret_cast<const bf16x4*>(row + e);
+      r = f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e + i < n) r[i] = (float)row[e + i];
+  }
+  return r;
+}
+template <typename E>
+__device__ __forceinline__ void store4(E* row, int e, int n, bool vec, const f32x4& v) {
+  if (vec && e + 3 < n) {
+    if constexpr (sizeof(E) == 4) {
+      *reinterpret_cast<f32x4*>(row + e) = v;
+    } else {
+      *reinterpret_cast<bf16x4*>(row + e) = bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (e + i < n) row[e + i] = (E)v[i];
+  }
+}
+
+template <typename EI, typename EO, int AK, int T>
+__global__ __launch_bounds__(kThreads) void k_entmax_rows(const EI* __restrict__ S, EO* __restrict__ Pout,
+                                                          float* __restrict__ tau_out,
+                                                          uint8_t* __restrict__ iters_out, RowParams P) {
+  __shared__ unsigned long long hist_all[kWaves][2 * kRowBins];
+  constexpr int NC = T > 0 ? T / 4 : 1;      // register chunks per lane
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = P.n;
+  const bool vec = P.vec != 0;
+  const int n_chunks = (n + 255) / 256;      // chunks of 256 elements (4 per lane)
+  unsigned long long* hr = hist_all[w];
+  const double beta = (double)P.beta;
+
+  for (long long r = (long long)blockIdx.x * kWaves + w; r < P.rows; r += (long long)gridDim.x * kWaves) {
+    const EI* row = S + r * n;
+    f32x4 xr[NC];
+    // the row's x values in registers (T > 0), its maximum and its count
+    float m = -INFINITY, cnt = 0.0f;
+    auto for_chunks = [&](auto&& fn) {
+      if constexpr (T > 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) fn(xr[c], 4 * (lane + 64 * c));
+      } else {
+        for (int c = 0; c < n_chunks; ++c) {
+          const int e = 4 * (lane + 64 * c);
+          f32x4 v = load4(row, e, n, vec) * P.scale;
+          fn(v, e);
+        }
+      }
+    };
+    if constexpr (T > 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) xr[c] = load4(row, 4 * (lane + 64 * c), n, vec) * P.scale;
+    }
+    for_chunks([&](const f32x4& v, int) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = fmax_nan(m, v[i]);
+        cnt += v[i] > -INFINITY ? 1.0f : 0.0f;
+      }
+    });
+    const float xmax = wave_max(m);
+    const float nv = wave_sum(cnt);
+    // bracket [max x - 1, max x - n^(1-alpha)], rounded outward
+    float lo = 0.0f, hi = 0.0f, tau = 0.0f;
+    const bool empty = !(nv > 0.0f);
+    if (!empty) {
+      const double dl = (double)xmax - 1.0;
+      lo = (float)dl;
+      if ((double)lo > dl) lo = nextafterf(lo, -INFINITY);
+      const double dh = (double)xmax - pow((double)nv, 1.0 - (double)P.alpha);
+      hi = (float)dh;
+      if ((double)hi < dh) hi = nextafterf(hi, INFINITY);
+      if (hi < lo) hi = lo;
+    }
+    if (P.mode == EA_TAU_HIST_HALLEY && !empty) {
+      for (int e = lane; e < 2 * kRowBins; e += kWave) hr[e] = 0ull;
+      __builtin_amdgcn_wave_barrier();
+      const float width = fmaxf(hi - lo, 1e-30f);
+      const float bin_scale = (float)kRowBins / width;
+      const float ysc = (float)(1u << P.hshift);
+      const unsigned ymax = (1u << P.hshift) - 1u;
+      for_chunks([&](const f32x4& v, int) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hist_add(hr, v[i] - lo, bin_scale, ysc, ymax, kRowBins);
+      });
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      hist_start<AK, kRowBins>(hr, width, xmax, P.hshift, P.beta, lo, hi, tau);
+    } else if (P.mode == EA_TAU_HALLEY_BISECT) {
+      tau = lo;
+    } else {
+      tau = 0.5f * (lo + hi);
+    }
+    // refinement sweeps: the same stopping rules as the attention kernel
+    bool conv = empty;
+    int iters = 0;
+    while (!conv) {
+      float F0 = 0, F1 = 0, F2 = 0, c2 = 0;
+      for_chunks([&](const f32x4& v, int) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ent<AK>::sweep(clamp01(v[i] - tau), P.beta, F0, F1, F2, c2);
+      });
+      F0 = wave_sum(F0);
+      F1 = wave_sum(F1);
+      if (P.mode != EA_TAU_BISECT && AK != AK20) F2 = wave_sum(F2);
+      ++iters;
+      const double f = (double)F0 - 1.0;
+      const double ulp = (double)FLT_EPSILON * fmax(1.0, fabs((double)tau));
+      const double fp = -beta * (double)F1;
+      const bool bisect = P.mode == EA_TAU_BISECT;
+      if (fabs(f) <= (double)P.tol + (bisect ? 0.0 : 2.0 * fabs(fp) * ulp)) break;
+      if (f > 0.0) lo = tau; else hi = tau;
+      const float wtol = bisect ? 1e-6f * fmaxf(1.0f, fabsf(tau)) : 4.0f * (float)ulp;
+      if (hi - lo <= wtol || iters >= P.max_iters) break;
+      double next = 0.5 * ((double)lo + (double)hi);
+      if (!bisect) {
+        const double fpp = (AK == AK20) ? 0.0 : beta * (beta - 1.0) * (double)F2;
+        const bool halley = fabs(f * fpp) < fp * fp;
+        const double th = halley ? (double)tau - 2.0 * f * fp / (2.0 * fp * fp - f * fpp) : (double)tau - f / fp;
+        if (fabs(th - (double)tau) <= 2.0 * ulp) break;
+        if (th > (double)lo && th < (double)hi) next = th;
+      }
+      float nt = (float)next;
+      if (!(nt > lo && nt < hi)) nt = lo + 0.5f * (hi - lo);
+      if (!(nt > lo && nt < hi)) break;
+      tau = nt;
+    }
+    // probabilities at the final tau
+    EO* prow = Pout + r * n;
+    const float ptau = empty ? INFINITY : tau;
+    for_chunks([&](const f32x4& v, int e) {
+      f32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float pp, u;
+        Ent<AK>::pu(clamp01(v[i] - ptau), P.beta, pp, u);
+        o[i] = pp;
+      }
+      store4(prow, e, n, vec, o);
+    });
+    if (lane == 0) {
+      tau_out[r] = empty ? NAN : tau;
+      if (iters_out) iters_out[r] = (uint8_t)min(iters, 255);
+    }
+  }
 }
 
 // =============================================================== host ===
@@ -2188,10 +2395,10 @@ size_t transposed_bytes(const Shape& s) {
   return s.esz == 4 ? align_up((size_t)s.BH * s.d * s.Np * s.esz, 256) : 0;
 }
 size_t row_bytes(const Shape& s) { return align_up((size_t)s.BH * s.N * sizeof(float), 256); }
-// one half per (row, 64-key tile), rows padded to a multiple of 32 tiles
-size_t tilemax_bytes(const Shape& s) {
-  const size_t ktp = (size_t)tilemax_row(s.n_kt);
-  return align_up((size_t)s.BH * s.N * ktp * sizeof(uint16_t), 256);
+// one byte per (32-query block, 64-key tile), rows padded to 64 tiles: the
+// size of the block mask, about N^2 / 2048 bytes per head
+size_t blkcode_bytes(const Shape& s) {
+  return align_up((size_t)s.BH * s.n_q32 * (size_t)blk_row(s.n_kt), 256);
 }
 
 // the block mask transposed, [BH][n_kt][n_q32 rounded up to 4] bytes
@@ -2200,9 +2407,9 @@ size_t maskt_bytes(const Shape& s) {
 }
 
 size_t workspace_bytes(const Shape& s) {
-  // forward: [V^T] | row maxima | tile maxima;
+  // forward: [V^T] | row maxima | block codes;
   // backward: [K^T | Q^T | dO^T] | delta | transposed mask
-  const size_t fwd = transposed_bytes(s) + row_bytes(s) + tilemax_bytes(s);
+  const size_t fwd = transposed_bytes(s) + row_bytes(s) + blkcode_bytes(s);
   const size_t bwd = 3 * transposed_bytes(s) + row_bytes(s) + maskt_bytes(s);
   const size_t ws = bwd > fwd ? bwd : fwd;
   return ws > 256 ? ws : 256;
@@ -2213,6 +2420,14 @@ int alpha_kind(float alpha) {
   if (alpha == 2.0f) return AK20;
   if (alpha == 1.25f) return AK125;
   return AKGEN;
+}
+
+// Fixed-point bits S of the histogram moments: N (2^(40-S) - 1) < 2^40 and
+// N (2^S - 1)^2 < 2^64 for every N <= 2^20; S = 24 up to N = 65536.
+int hist_shift(int N) {
+  int L = 1;
+  while ((1 << L) < N) ++L;
+  return L <= 16 ? 24 : 40 - L;
 }
 
 Params make_params(const ea_desc* desc, const Shape& s, float alpha, int causal) {
@@ -2233,6 +2448,7 @@ Params make_params(const ea_desc* desc, const Shape& s, float alpha, int causal)
   P.tol = desc->tol > 0.0f ? desc->tol : 1e-6f;
   P.out_bf16 = desc->out_dtype == EA_BF16 ? 1 : 0;
   P.pair_qt = 0;
+  P.hshift = hist_shift(s.N);
   return P;
 }
 
@@ -2264,6 +2480,8 @@ struct StageTimer {
   }
 };
 
+// Dynamic LDS above the default 64 KB must be allowed per kernel before its
+// first launch.
 template <typename F>
 int set_lds(F* fn, size_t bytes) {
   if (bytes > 160 * 1024) return EA_ERR_UNSUPPORTED;
@@ -2275,10 +2493,23 @@ int set_lds(F* fn, size_t bytes) {
   return EA_OK;
 }
 
+// Launches kernel k and returns the launch's own status (an error left by an
+// earlier, unrelated HIP call is neither reported nor cleared).
+template <typename... KA, typename... CA>
+int launch(void (*k)(KA...), dim3 grid, dim3 block, size_t lds, hipStream_t st, CA... args) {
+  auto go = [&](KA... a) {
+    void* argv[] = {static_cast<void*>(&a)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, argv, lds, st);
+  };
+  return go(args...) == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+}
+
 template <typename E, int D, int AK>
 int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const void* v, void* out,
                float* tau, uint8_t* mask, uint8_t* iters, void* ws, hipStream_t st, StageTimer tm) {
   constexpr bool kTr = sizeof(E) == 2;
+  constexpr int KS = row_stride<E, D>();
+  constexpr int BINS = 16;
   const E* Q = static_cast<const E*>(q);
   const E* K = static_cast<const E*>(k);
   const E* V = static_cast<const E*>(v);
@@ -2286,53 +2517,58 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   char* w = static_cast<char*>(ws);
   E* Vt = reinterpret_cast<E*>(w);
   float* rowmax = reinterpret_cast<float*>(w + transposed_bytes(s));
-  uint16_t* tilemax = reinterpret_cast<uint16_t*>(w + transposed_bytes(s) + row_bytes(s));
+  uint8_t* blkc = reinterpret_cast<uint8_t*>(w + transposed_bytes(s) + row_bytes(s));
+
+  // every LDS size is checked and allowed before anything is enqueued
+  const size_t rm_lds = kTr ? (size_t)2 * kRowmaxTPS * DirectTile<D>::BYTES : (size_t)2 * kBK * KS;
+  const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)tau_region_bytes<E, D>(BINS) + 4 * kChunk +
+                         (size_t)3 * kWaves * ((s.n_kt + 31) / 32) * 4 + 64;
+  constexpr int VT = D * (kBK * (int)sizeof(E) + 16);
+  const size_t pv_lds = (size_t)2 * kBK * KS + (size_t)2 * VT + 4 * kChunk + 16;
+  auto ktau = k_tau<E, D, AK, BINS>;
+  auto kpv = k_pv<E, D, AK>;
   int rc;
+  if constexpr (kTr) {
+    if ((rc = set_lds(k_rowmax16<D>, rm_lds)) != EA_OK) return rc;
+  } else {
+    if ((rc = set_lds(k_rowmax<E, D>, rm_lds)) != EA_OK) return rc;
+    if ((rc = set_lds(kpv, pv_lds)) != EA_OK) return rc;
+  }
+  if ((rc = set_lds(ktau, tau_lds)) != EA_OK) return rc;
 
   tm.begin(EA_STAGE_FWD_PREP);
-  if constexpr (!kTr)
-    hipLaunchKernelGGL(k_transpose<E>, dim3(s.Np / 64, D / 64, s.BH), dim3(256), 0, st, V, Vt, s.N, D, s.Np);
+  if constexpr (!kTr) {
+    if ((rc = launch(k_transpose<E>, dim3(s.Np / 64, D / 64, s.BH), dim3(256), 0, st, V, Vt, s.N, D, s.Np)) != EA_OK)
+      return rc;
+  }
   tm.end(EA_STAGE_FWD_PREP);
 
-  constexpr int KS = row_stride<E, D>();
-  if constexpr (sizeof(E) == 2) {
-    const size_t rm_lds = (size_t)2 * kRowmaxTPS * DirectTile<D>::BYTES;
-    auto krm = k_rowmax16<D>;
-    if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
-    tm.begin(EA_STAGE_ROWMAX);
+  tm.begin(EA_STAGE_ROWMAX);
+  if constexpr (kTr) {
     P.pair_qt = pair_query_tiles(s, P.causal) ? 1 : 0;
     const int units = P.pair_qt ? (s.n_qt256 + 1) / 2 : s.n_qt256;
-    hipLaunchKernelGGL(krm, dim3(units * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, tilemax);
-    tm.end(EA_STAGE_ROWMAX);
+    rc = launch(k_rowmax16<D>, dim3(units * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, blkc);
   } else {
-    const size_t rm_lds = (size_t)2 * kBK * KS;
-    auto krm = k_rowmax<E, D>;
-    if ((rc = set_lds(krm, rm_lds)) != EA_OK) return rc;
-    tm.begin(EA_STAGE_ROWMAX);
-    hipLaunchKernelGGL(krm, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, tilemax);
-    tm.end(EA_STAGE_ROWMAX);
+    rc = launch(k_rowmax<E, D>, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, blkc);
   }
+  if (rc != EA_OK) return rc;
+  tm.end(EA_STAGE_ROWMAX);
 
-  constexpr int BINS = 16;
-  const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)tau_region_bytes<E, D>(BINS) + 4 * kChunk +
-                         (size_t)2 * kWaves * ((s.n_kt + 31) / 32) * 4 + 64;
-  auto ktau = k_tau<E, D, AK, BINS>;
-  if ((rc = set_lds(ktau, tau_lds)) != EA_OK) return rc;
   const dim3 g(s.n_qt128 * s.BH);
   tm.begin(EA_STAGE_TAU);   // bf16: tau, block mask and P V in one kernel
-  hipLaunchKernelGGL(ktau, g, dim3(kThreads), tau_lds, st, Q, K, V, rowmax, tilemax, P, tau, mask, iters, out);
+  if ((rc = launch(ktau, g, dim3(kThreads), tau_lds, st, Q, K, V, (const float*)rowmax, (const uint8_t*)blkc, P,
+                   tau, mask, iters, out)) != EA_OK)
+    return rc;
   tm.end(EA_STAGE_TAU);
 
   tm.begin(EA_STAGE_PV);   // empty for bf16 (fused above)
   if constexpr (!kTr) {
-    constexpr int VT = D * (kBK * (int)sizeof(E) + 16);
-    const size_t pv_lds = (size_t)2 * kBK * KS + (size_t)2 * VT + 4 * kChunk + 16;
-    auto kpv = k_pv<E, D, AK>;
-    if ((rc = set_lds(kpv, pv_lds)) != EA_OK) return rc;
-    hipLaunchKernelGGL(kpv, g, dim3(kThreads), pv_lds, st, Q, K, Vt, tau, mask, P, out);
+    if ((rc = launch(kpv, g, dim3(kThreads), pv_lds, st, Q, K, (const E*)Vt, (const float*)tau,
+                     (const uint8_t*)mask, P, out)) != EA_OK)
+      return rc;
   }
   tm.end(EA_STAGE_PV);
-  return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+  return EA_OK;
 }
 
 template <typename E, int D, int AK>
@@ -2352,36 +2588,76 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
   E* dOt = reinterpret_cast<E*>(w + 2 * tb);
   float* delta = reinterpret_cast<float*>(w + 3 * tb);
   uint8_t* maskT = reinterpret_cast<uint8_t*>(w + 3 * tb + row_bytes(s));
-  int rc;
-  tm.begin(EA_STAGE_BWD_PREP);
-  if constexpr (!kTr) {
-    const dim3 tg(s.Np / 64, D / 64, s.BH);
-    hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, K, Kt, s.N, D, s.Np);
-    hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, Q, Qt, s.N, D, s.Np);
-    hipLaunchKernelGGL(k_transpose<E>, tg, dim3(256), 0, st, dO, dOt, s.N, D, s.Np);
-  }
-  tm.end(EA_STAGE_BWD_PREP);
 
   constexpr int KS = row_stride<E, D>();
   constexpr int TT = kTr ? 0 : D * (kBK * (int)sizeof(E) + 16);
   constexpr int NB = (2 * (2 * kBK * KS + TT) + 4 * kChunk + 16) <= 160 * 1024 ? 2 : 1;
   const size_t dq_lds = (size_t)NB * (2 * kBK * KS + TT) + 4 * kChunk + 16;
-  auto kdq = k_bwd_dq<E, D, AK, NB>;
-  if ((rc = set_lds(kdq, dq_lds)) != EA_OK) return rc;
-  tm.begin(EA_STAGE_DQ);
-  hipLaunchKernelGGL(kdq, dim3(s.n_qt128 * s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO, Kt, tau, mask,
-                     P, delta, maskT, dq);
-  tm.end(EA_STAGE_DQ);
-
   const size_t kv_lds = (size_t)kv_stages<E, D>() * kv_step_bytes<E, D>() + 4 * kChunk + 16 +
                         (kTr && D == 128 ? (size_t)4 * kBQ * KS : 0);   // the K rows (bf16, d = 128)
+  auto kdq = k_bwd_dq<E, D, AK, NB>;
   auto kkv = k_bwd_dkdv<E, D, AK>;
+  int rc;
+  if ((rc = set_lds(kdq, dq_lds)) != EA_OK) return rc;
   if ((rc = set_lds(kkv, kv_lds)) != EA_OK) return rc;
+
+  tm.begin(EA_STAGE_BWD_PREP);
+  if constexpr (!kTr) {
+    const dim3 tg(s.Np / 64, D / 64, s.BH);
+    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, K, Kt, s.N, D, s.Np)) != EA_OK) return rc;
+    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, Q, Qt, s.N, D, s.Np)) != EA_OK) return rc;
+    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, dO, dOt, s.N, D, s.Np)) != EA_OK) return rc;
+  }
+  tm.end(EA_STAGE_BWD_PREP);
+
+  tm.begin(EA_STAGE_DQ);
+  if ((rc = launch(kdq, dim3(s.n_qt128 * s.BH), dim3(kThreads), dq_lds, st, Q, K, V, dO, (const E*)Kt, tau,
+                   mask, P, delta, maskT, dq)) != EA_OK)
+    return rc;
+  tm.end(EA_STAGE_DQ);
+
   tm.begin(EA_STAGE_DKDV);
-  hipLaunchKernelGGL(kkv, dim3(s.n_kt128 * s.BH), dim3(kThreads), kv_lds, st, Q, K, V, dO, Qt, dOt, tau,
-                     delta, maskT, P, dk, dv);
+  if ((rc = launch(kkv, dim3(s.n_kt128 * s.BH), dim3(kThreads), kv_lds, st, Q, K, V, dO, (const E*)Qt,
+                   (const E*)dOt, tau, (const float*)delta, (const uint8_t*)maskT, P, dk, dv)) != EA_OK)
+    return rc;
   tm.end(EA_STAGE_DKDV);
-  return hipGetLastError() == hipSuccess ? EA_OK : EA_ERR_LAUNCH;
+  return EA_OK;
+}
+
+// ------------------------------------------------- row transform host ---
+int check_rows_desc(const ea_rows_desc* d) {
+  if (!d) return EA_ERR_NULL;
+  if (d->rows < 0 || d->n < 1 || d->n > kMaxN || d->rows > ((long long)1 << 40) / d->n) return EA_ERR_SHAPE;
+  if ((d->in_dtype != EA_F32 && d->in_dtype != EA_BF16) || (d->out_dtype != EA_F32 && d->out_dtype != EA_BF16))
+    return EA_ERR_DTYPE;
+  if (d->tau_mode < EA_TAU_HIST_HALLEY || d->tau_mode > EA_TAU_BISECT) return EA_ERR_UNSUPPORTED;
+  if (d->max_iters < 0 || d->max_iters > 250) return EA_ERR_UNSUPPORTED;
+  if (!(d->tol >= 0.0f) || !(d->tol < 1.0f)) return EA_ERR_UNSUPPORTED;
+  return EA_OK;
+}
+
+template <typename EI, typename EO, int AK>
+int launch_rows(const ea_rows_desc* d, RowParams P, const void* s, void* p, float* tau, uint8_t* iters,
+                hipStream_t st) {
+  if (d->rows == 0) return EA_OK;
+  const long long groups = (d->rows + kWaves - 1) / kWaves;
+  const dim3 g((unsigned)(groups < 8192 ? groups : 8192));
+  const EI* S = static_cast<const EI*>(s);
+  EO* Po = static_cast<EO*>(p);
+  if (d->n <= 1024) return launch(k_entmax_rows<EI, EO, AK, 16>, g, dim3(kThreads), 0, st, S, Po, tau, iters, P);
+  if (d->n <= 4096) return launch(k_entmax_rows<EI, EO, AK, 64>, g, dim3(kThreads), 0, st, S, Po, tau, iters, P);
+  return launch(k_entmax_rows<EI, EO, AK, 0>, g, dim3(kThreads), 0, st, S, Po, tau, iters, P);
+}
+
+template <typename EI, typename EO>
+int dispatch_rows_ak(float alpha, const ea_rows_desc* d, RowParams P, const void* s, void* p, float* tau,
+                     uint8_t* iters, hipStream_t st) {
+  switch (alpha_kind(alpha)) {
+    case AK15: return launch_rows<EI, EO, AK15>(d, P, s, p, tau, iters, st);
+    case AK20: return launch_rows<EI, EO, AK20>(d, P, s, p, tau, iters, st);
+    case AK125: return launch_rows<EI, EO, AK125>(d, P, s, p, tau, iters, st);
+    default: return launch_rows<EI, EO, AKGEN>(d, P, s, p, tau, iters, st);
+  }
 }
 
 #define EA_DISPATCH(FN, ...)                                                          \
@@ -2483,6 +2759,34 @@ int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, in
   hipStream_t hs = static_cast<hipStream_t>(stream);
   EA_DISPATCH(launch_bwd, s, P, q, k, v, dout, tau, block_mask, dq, dk, dv, ws, hs,
               StageTimer{desc->events, hs});
+}
+
+int entmax_rows(const void* s, float alpha, void* p, float* tau, uint8_t* tau_iters, const ea_rows_desc* desc,
+                void* stream) {
+  int st = check_rows_desc(desc);
+  if (st != EA_OK) return st;
+  if ((st = check_alpha(alpha)) != EA_OK) return st;
+  if (desc->rows > 0) {
+    if (!s || !p || !tau) return EA_ERR_NULL;
+    if (misaligned(s) || misaligned(p) || misaligned(tau)) return EA_ERR_ALIGN;
+  }
+  RowParams P;
+  P.rows = desc->rows;
+  P.n = desc->n;
+  P.mode = desc->tau_mode;
+  P.max_iters = desc->max_iters > 0 ? desc->max_iters : (desc->tau_mode == EA_TAU_BISECT ? 40 : 12);
+  P.hshift = hist_shift(desc->n);
+  P.vec = desc->n % 4 == 0 ? 1 : 0;
+  P.alpha = alpha;
+  P.scale = (float)((double)alpha - 1.0);
+  P.beta = (float)(1.0 / ((double)alpha - 1.0));
+  P.tol = desc->tol > 0.0f ? desc->tol : 1e-6f;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool ib = desc->in_dtype == EA_BF16, ob = desc->out_dtype == EA_BF16;
+  if (ib && ob) return dispatch_rows_ak<__bf16, __bf16>(alpha, desc, P, s, p, tau, tau_iters, hs);
+  if (ib) return dispatch_rows_ak<__bf16, float>(alpha, desc, P, s, p, tau, tau_iters, hs);
+  if (ob) return dispatch_rows_ak<float, __bf16>(alpha, desc, P, s, p, tau, tau_iters, hs);
+  return dispatch_rows_ak<float, float>(alpha, desc, P, s, p, tau, tau_iters, hs);
 }
 
 const char* entmax_attn_strerror(int status) {

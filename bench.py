@@ -38,6 +38,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "adaptive_sparse_flash_amd", "csrc", "entmax_attn.hip")
 COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "k_rowmax16_planted_16k_hbm_counters.md")
+TRACE_SUMMARY = os.path.join(ROOT, "profiles", "k_rowmax16_planted_16k_kernel_trace.md")
 
 
 def recorded_traffic(summary: str = COUNTER_SUMMARY, src: str = KERNEL_SRC):
@@ -140,6 +141,155 @@ def cpu_baseline(w, x, max_heads: int, min_seconds: float = 10.0):
                       f"(full N={w.N}), {dt:.1f} s; rate scaled to the whole step"}
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def recorded_kernel_us(summary: str = TRACE_SUMMARY, src: str = KERNEL_SRC):
+    """Average duration (us) of the row-max kernel in the committed rocprofv3
+    kernel trace, or None when the trace was taken on a different source."""
+    try:
+        text = open(summary).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(\w+) = (\S+)$", text, re.M))
+    if vals.get("kernel_source_sha256") != digest or "rowmax_avg_us" not in vals:
+        return None
+    return float(vals["rowmax_avg_us"])
+
+
+def describe(w) -> str:
+    return (f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
+            f"{'causal' if w.causal else 'non-causal'} alpha={w.alpha} {w.gen}"
+            + (f" span={w.span} strength={w.strength}" if w.gen == "planted" else f" scale={w.scale}"))
+
+
+def element_sparsity_gpu(q, k, tau, alpha, causal, rows=4096):
+    """Share of visible score entries with zero probability (x <= tau), from
+    float32 scores recomputed by torch on the GPU chunk by chunk (a statistic
+    for the report, not part of the attention path)."""
+    import torch
+
+    B, H, N, d = q.shape
+    nz, vis = 0, 0
+    scale = (alpha - 1.0) / float(np.sqrt(d))
+    for b in range(B):
+        for h in range(H):
+            kf = k[b, h].float()
+            for r0 in range(0, N, rows):
+                r1 = min(N, r0 + rows)
+                x = (q[b, h, r0:r1].float() @ kf.T) * scale
+                keep = x > tau[b, h, r0:r1, None]
+                if causal:
+                    ii = torch.arange(r0, r1, device=x.device)[:, None]
+                    jj = torch.arange(N, device=x.device)[None, :]
+                    keep &= jj <= ii
+                    vis += (r1 - r0) * (r0 + r1 + 1) // 2
+                else:
+                    vis += (r1 - r0) * N
+                nz += int(keep.sum().item())
+    return 1.0 - nz / max(vis, 1)
+
+
+class Runner:
+    """One workload's device inputs and buffers; measure() times fwd+bwd steps
+    with HIP events per stage."""
+
+    def __init__(self, A, torch, w, x, tau_mode, dev):
+        self.A, self.torch, self.w = A, torch, w
+        dt_in = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.q, self.k, self.v, self.do = (torch.from_numpy(x[n]).to(dt_in).to(dev)
+                                           for n in ("q", "k", "v", "dout"))
+        self.bufs = A.Buffers(w.B, w.H, w.N, w.d, dt_in, dt_in, tau_mode, device=dev)
+
+    def step(self):
+        w = self.w
+        self.bufs.forward(self.q, self.k, self.v, w.alpha, w.causal)
+        self.bufs.backward(self.q, self.k, self.v, self.do, w.alpha, w.causal)
+
+    def measure(self, steps, warmup):
+        torch, A = self.torch, self.A
+        ns = A.binding.EA_NUM_STAGES
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        ev = HipEvents(2 * ns * steps)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.bufs.desc.events = ev.block(s, 2 * ns)
+            self.step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        self.bufs.desc.events = None
+        stage_ms = {}
+        for si, name in enumerate(A.binding.STAGES):
+            vals = [ev.elapsed_ms(s * 2 * ns + 2 * si, s * 2 * ns + 2 * si + 1) for s in range(steps)]
+            stage_ms[name] = float(np.mean(vals))
+        ev.close()
+        w = self.w
+        mask = self.bufs.mask.cpu().numpy().reshape(w.B * w.H, *self.bufs.mask.shape[2:])
+        iters = self.bufs.iters.cpu().numpy()
+        ms = (t1 - t0) / steps * 1e3
+        return {"ms_per_step": ms, "tflops": dense_equiv_flops(w) / (ms * 1e-3) / 1e12,
+                "block_sparsity_32x64": block_sparsity(mask, w.N, w.causal, 1),
+                "block_sparsity_128x64": block_sparsity(mask, w.N, w.causal, 4),
+                "tau_iters_mean": float(iters.mean()), "tau_iters_max": int(iters.max()),
+                "stage_ms": stage_ms}
+
+    def element_sparsity(self):
+        return element_sparsity_gpu(self.q, self.k, self.bufs.tau, self.w.alpha, self.w.causal)
+
+    def close(self):
+        del self.q, self.k, self.v, self.do, self.bufs
+        self.torch.cuda.empty_cache()
+
+
+def bench_transform(A, torch, G, dev, alpha=1.5, reps=10):
+    """Stand-alone row-wise entmax (entmax_rows) on fp32 score rows
+    s ~ N(0, 2^2) (x ~ N(0, 1) at alpha = 1.5): per tau mode the time per
+    launch (HIP events on the launch stream, `reps` launches after 2 warm-up
+    ones), algorithmic HBM bytes per second (read s, write p, tau and the
+    sweep counts once) against the 8 TB/s peak, and sweeps per row."""
+    res = []
+    for rows, n in ((16384, 4096), (4096, 16384)):
+        s = torch.from_numpy(G.make_score_rows(rows, n, scale=2.0, seed=1)).to(dev)
+        p = torch.empty_like(s)
+        tau = torch.empty(rows, dtype=torch.float32, device=dev)
+        it = torch.empty(rows, dtype=torch.uint8, device=dev)
+        byt = rows * n * 8 + rows * 5
+        point = {"rows": rows, "n": n, "path": "registers" if n <= 4096 else "streamed", "modes": {}}
+        for mode in ("hist", "halley", "bisect"):
+            desc = A.make_rows_desc(rows, n, torch.float32, torch.float32, mode)
+            for _ in range(2):
+                A.entmax_rows(s, alpha, p, tau, it, desc)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                A.entmax_rows(s, alpha, p, tau, it, desc)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            itc = it.cpu().numpy()
+            point["modes"][mode] = {"ms": ms, "gbs": byt / (ms * 1e-3) / 1e9,
+                                    "hbm_frac": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "sweeps_mean": float(itc.mean()), "sweeps_max": int(itc.max())}
+        b = point["modes"]["bisect"]
+        for mode in ("hist", "halley"):
+            point["modes"][mode]["speedup_vs_bisect"] = b["ms"] / point["modes"][mode]["ms"]
+            point["modes"][mode]["sweep_ratio_vs_bisect"] = b["sweeps_mean"] / max(point["modes"][mode]["sweeps_mean"], 1e-9)
+        res.append(point)
+        del s, p
+    return {"alpha": alpha, "scores": "fp32 s ~ N(0, 4), dense rows", "points": res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,6 +305,11 @@ def main():
     ap.add_argument("--alpha", type=float, default=None, help="override the workload's alpha")
     ap.add_argument("--scale", type=float, default=None,
                     help="iid workloads: standard deviation c of Q and K (sets the sparsity)")
+    ap.add_argument("--n", type=int, default=None, help="override the sequence length")
+    ap.add_argument("--heads", type=int, default=None, help="override the head count")
+    ap.add_argument("--extras", type=int, default=1,
+                    help="1: also measure the sparsity sweep, the long-context tau modes and the "
+                         "sequence-length scaling (after the headline timing); 0: headline only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 512 MiB device copy first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -167,24 +322,16 @@ def main():
     import adaptive_sparse_flash_amd as A
     from gen import inputs as G
 
+    torch.backends.cuda.matmul.allow_tf32 = False
     over = {}
-    if args.strength is not None:
-        over["strength"] = args.strength
-    if args.alpha is not None:
-        over["alpha"] = args.alpha
-    if args.scale is not None:
-        over["scale"] = args.scale
+    for key, val in (("strength", args.strength), ("alpha", args.alpha), ("scale", args.scale),
+                     ("N", args.n), ("H", args.heads)):
+        if val is not None:
+            over[key] = val
     w = G.workload(args.workload, **over)
     x = G.make_inputs(w)
-    dt_in = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
-    q, k, v, do = (torch.from_numpy(x[n]).to(dt_in).to(dev) for n in ("q", "k", "v", "dout"))
-    bufs = A.Buffers(w.B, w.H, w.N, w.d, dt_in, dt_in, args.tau_mode, device=dev)
-    ns = A.binding.EA_NUM_STAGES if hasattr(A.binding, "EA_NUM_STAGES") else 6
-
-    def step():
-        bufs.forward(q, k, v, w.alpha, w.causal)
-        bufs.backward(q, k, v, do, w.alpha, w.causal)
+    run = Runner(A, torch, w, x, args.tau_mode, dev)
 
     if args.copy_calibration:
         # 512 MiB read + 512 MiB written by one elementwise copy kernel
@@ -195,32 +342,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    ev = HipEvents(2 * ns * args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        bufs.desc.events = ev.block(s, 2 * ns)
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    bufs.desc.events = None
-    ms = (t1 - t0) / args.steps * 1e3
-    stage_ms = {}
-    for si, name in enumerate(A.binding.STAGES):
-        vals = [ev.elapsed_ms(s * 2 * ns + 2 * si, s * 2 * ns + 2 * si + 1) for s in range(args.steps)]
-        stage_ms[name] = float(np.mean(vals))
-    ev.close()
-
-    mask = bufs.mask.cpu().numpy().reshape(w.B * w.H, *bufs.mask.shape[2:])
-    iters = bufs.iters.cpu().numpy()
-    sp32 = block_sparsity(mask, w.N, w.causal, 1)
-    sp128 = block_sparsity(mask, w.N, w.causal, 4)
-    flops = dense_equiv_flops(w)
-    value = flops / (ms * 1e-3) / 1e12
+    # ---- headline: exactly `steps` timed steps after `warmup` untimed ones
+    head = run.measure(args.steps, args.warmup)
+    ms, stage_ms = head["ms_per_step"], head["stage_ms"]
+    value = head["tflops"]
+    elem_sp = run.element_sparsity()
+    ws_bytes = int(run.bufs.ws.numel())
 
     # Dominant kernel: the row-max sweep (k_rowmax16 for bf16), the one full
     # score sweep.  Its algorithmic work per launch is 2*d flops per visible
@@ -229,13 +356,15 @@ def main():
     sweep_flops = 2.0 * w.d * vis * w.B * w.H
     rm_ms = stage_ms["rowmax"]
     achieved = sweep_flops / (rm_ms * 1e-3) / 1e12
-    default_config = (args.workload == "planted_16k" and args.strength is None and args.alpha is None
-                      and args.scale is None and args.tau_mode == "hist")
+    default_config = (args.workload == "planted_16k" and not over and args.tau_mode == "hist")
+    rec_us = recorded_kernel_us() if default_config else None
     roofline = {"bound": "mfma", "kernel": "k_rowmax16" if w.dtype == "bf16" else "k_rowmax",
                 "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                 "traffic": recorded_traffic() if default_config else None,
-                "flops_per_launch": sweep_flops, "launch_ms": rm_ms}
+                "flops_per_launch": sweep_flops, "launch_ms": rm_ms,
+                "rocprof_avg_us": rec_us,
+                "frac_rocprof": (sweep_flops / (rec_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS) if rec_us else None}
 
     line = {
         "metric": "fwd+bwd dense-equivalent TFLOP/s (alpha=1.5 entmax attention, N=16k, 1 GPU)",
@@ -251,20 +380,70 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} "
-                        f"{'causal' if w.causal else 'non-causal'} alpha={w.alpha} {w.gen}"
-                        + (f" span={w.span} strength={w.strength}" if w.gen == "planted" else f" scale={w.scale}"),
+            "workload": describe(w),
             "tau_mode": args.tau_mode,
-            "block_sparsity_32x64": sp32,
-            "block_sparsity_128x64": sp128,
-            "tau_iters_mean": float(iters.mean()),
-            "tau_iters_max": int(iters.max()),
+            "block_sparsity_32x64": head["block_sparsity_32x64"],
+            "block_sparsity_128x64": head["block_sparsity_128x64"],
+            "element_sparsity": elem_sp,
+            "tau_iters_mean": head["tau_iters_mean"],
+            "tau_iters_max": head["tau_iters_max"],
             "stage_ms": stage_ms,
+            "workspace_bytes": ws_bytes,
         },
         "roofline": roofline,
     }
+    run.close()
+
+    if args.extras and default_config:
+        # ---- throughput vs block sparsity: the same generator at weaker query
+        # strengths (5 timed steps each after 2 warm-up steps)
+        sweep = [dict(strength=w.strength, **{k_: head[k_] for k_ in (
+            "ms_per_step", "tflops", "block_sparsity_32x64", "block_sparsity_128x64",
+            "tau_iters_mean", "tau_iters_max", "stage_ms")}, element_sparsity=elem_sp)]
+        for a in (0.5, 0.4, 0.3):
+            wa = w.with_(strength=a)
+            r = Runner(A, torch, wa, G.make_inputs(wa), "hist", dev)
+            m = r.measure(5, 2)
+            m["element_sparsity"] = r.element_sparsity()
+            m["strength"] = a
+            sweep.append(m)
+            r.close()
+        line["sparsity_sweep"] = sweep
+
+        # ---- long-context workload: the three tau modes (5 timed steps each)
+        wl = G.workload("planted_32k")
+        xl = G.make_inputs(wl)
+        modes = {}
+        for mode in ("hist", "halley", "bisect"):
+            r = Runner(A, torch, wl, xl, mode, dev)
+            m = r.measure(5, 2)
+            modes[mode] = {k_: m[k_] for k_ in ("ms_per_step", "tflops", "tau_iters_mean", "tau_iters_max",
+                                                "block_sparsity_32x64")}
+            modes[mode]["tau_stage_ms"] = m["stage_ms"]["tau"]
+            r.close()
+        line["tau_modes"] = {"workload": describe(wl), **modes}
+        del xl
+
+        # ---- sequence-length scaling, one head (3 timed steps each)
+        scal = []
+        for n in (32768, 65536, 131072):
+            wn = G.workload("planted_32k", H=1, N=n)
+            r = Runner(A, torch, wn, G.make_inputs(wn), "hist", dev)
+            m = r.measure(3, 1)
+            scal.append({"N": n, "ms_per_step": m["ms_per_step"], "tflops": m["tflops"],
+                         "block_sparsity_32x64": m["block_sparsity_32x64"],
+                         "tau_iters_mean": m["tau_iters_mean"],
+                         "workspace_bytes": int(r.bufs.ws.numel()),
+                         "stage_ms": m["stage_ms"]})
+            r.close()
+        line["seq_scaling"] = {"workload": "planted span 512, B=1 H=1 d=128 bf16 causal alpha=1.5",
+                               "points": scal}
+        line["transform"] = bench_transform(A, torch, G, dev)
+
     if args.cpu_heads > 0:
-        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
+        cb = cpu_baseline(w, x, args.cpu_heads)
+        cb["cpu_model"] = cpu_model()
+        line["cpu_baseline"] = cb
     print(json.dumps(line))
 
 

@@ -16,6 +16,10 @@ for it):
                k = (i // span) % 64;  Q_i = a * c_k + N(0, I),
                K_i = c_k + 0.3 * N(0, I), V, dO ~ N(0, 1).  With a = 3 this
                yields >95 % block sparsity at 64-key tiles.
+* ``tied``     many exactly equal keys: one centroid c = sqrt(d) * u;
+               Q_i = a * c + N(0, I); K_j = c for j < ties (identical rows),
+               K_j ~ N(0, I) after; V, dO ~ N(0, 1).  Rows that see more than
+               65536 of the tied keys put them all in one histogram bin.
 
 Draw order (fixed, one ``standard_normal`` call per tensor, PCG64 via
 ``numpy.random.default_rng(seed)``): centroids (planted only), Q, K, V, dO.
@@ -32,6 +36,7 @@ __all__ = [
     "WORKLOADS",
     "bf16_round",
     "make_inputs",
+    "make_score_rows",
     "workload",
 ]
 
@@ -46,12 +51,6 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     lsb = (u >> np.uint64(16)) & np.uint64(1)
     u = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16) << np.uint64(16)
     return u.astype(np.uint32).view(np.float32).reshape(f.shape)
-
-
-def bf16_bits(x32: np.ndarray) -> np.ndarray:
-    """Upper 16 bits of float32 values that are already bf16-exact (uint16 array)."""
-    f = np.ascontiguousarray(x32, dtype=np.float32)
-    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 @dataclass(frozen=True)
@@ -71,6 +70,7 @@ class Workload:
     scale_v: bool = False
     strength: float = 3.0  # planted: Q = strength * centroid + noise
     span: int = 256        # planted: tokens per cluster run
+    ties: int = 0          # tied: number of leading identical keys
     backward: bool = True
     seed: int = 0
     extra: dict = field(default_factory=dict)
@@ -102,6 +102,14 @@ def make_inputs(w: Workload, heads: slice | None = None) -> dict:
         k = c_tok + 0.3 * rng.standard_normal(shape)
         v = rng.standard_normal(shape)
         do = rng.standard_normal(shape)
+    elif w.gen == "tied":
+        g = rng.standard_normal((w.B, w.H, 1, w.d))
+        cent = np.sqrt(w.d) * g / np.linalg.norm(g, axis=-1, keepdims=True)
+        q = w.strength * cent + rng.standard_normal(shape)
+        k = rng.standard_normal(shape)
+        k[:, :, :w.ties, :] = cent
+        v = rng.standard_normal(shape)
+        do = rng.standard_normal(shape)
     elif w.gen == "iid":
         q = w.scale * rng.standard_normal(shape)
         k = w.scale * rng.standard_normal(shape)
@@ -119,6 +127,20 @@ def make_inputs(w: Workload, heads: slice | None = None) -> dict:
             a = a.reshape(w.B * w.H, w.N, w.d)[heads]
         out[name] = np.ascontiguousarray(a)
     return out
+
+
+def make_score_rows(rows: int, n: int, scale: float = 1.0, seed: int = 0, dtype: str = "f32",
+                    masked: float = 0.0) -> np.ndarray:
+    """Score rows for the stand-alone entmax transform: s ~ N(0, scale^2),
+    float32 [rows, n] rounded to the storage dtype; a share `masked` of the
+    entries (drawn after the scores) is set to -inf."""
+    rng = np.random.default_rng(seed)
+    s = (scale * rng.standard_normal((rows, n))).astype(np.float32)
+    if dtype == "bf16":
+        s = bf16_round(s)
+    if masked > 0.0:
+        s[rng.random((rows, n)) < masked] = -np.inf
+    return np.ascontiguousarray(s)
 
 
 # The five reference workloads.  Index 0 is the small fp32 parity case; the

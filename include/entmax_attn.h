@@ -101,11 +101,13 @@ typedef struct {
 #define EA_NUM_STAGES      7
 
 /* Bytes of device workspace both entry points need for `desc`: one float per
- * row; (forward) each row's maximum over every 64-key tile, as a half rounded
- * up, rows padded to a multiple of 32 tiles (B*H*N*ceil(N/2048)*64 bytes, about
- * 1/128 of an fp32 score matrix); (backward) the block mask transposed, one
- * byte per (64-key tile, 32-query row); and for fp32 inputs transposed copies
- * of V (forward) or of K, Q, dO (backward).  Returns 0 for an invalid desc. */
+ * row; (forward) one byte per (32-query block, 64-key tile), rows padded to 64
+ * tiles -- the size of the block mask, B*H*ceil(N/32)*ceil(N/64) bytes, never
+ * a score matrix (the fused kernel's memory grows like its inputs and its
+ * block mask: "AdaSplash: Adaptive Sparse Flash Attention", "AdaSplash: Fused
+ * GPU Kernel for Attention"); (backward) the block mask transposed; and for
+ * fp32 inputs transposed copies of V (forward) or of K, Q, dO (backward).
+ * Returns 0 for an invalid desc. */
 size_t entmax_attn_workspace_bytes(const ea_desc* desc);
 
 /* Shape of block_mask: [B, H, n_qt, n_kt] bytes with n_qt = ceil(N/bm),
@@ -139,6 +141,40 @@ int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, in
                     const void* dout, const float* tau, const uint8_t* block_mask,
                     void* dq, void* dk, void* dv,
                     const ea_desc* desc, void* ws, size_t ws_bytes, void* stream);
+
+/* Row-wise alpha-entmax of materialised score rows, without attention
+ * ("AdaSplash: Adaptive Sparse Flash Attention", "Accelerated Alpha-Entmax
+ * Transformation": the entmax transform whose threshold Halley-bisection
+ * finds in far fewer iterations than bisection; "AdaSplash-2: The Transformer
+ * Revolution We Didn't See Coming", "Sparse Attention Makes Waves": the
+ * histogram start).  For each row r:
+ *   x_j = (alpha - 1) s_rj,  tau_r: sum_j [x_j - tau_r]_+^(1/(alpha-1)) = 1,
+ *   p_rj = [x_j - tau_r]_+^(1/(alpha-1)).
+ * -inf scores are masked entries (p = 0, not counted); a row with no finite
+ * score gets tau = NaN and p = 0.  tau_mode selects the start and the steps
+ * exactly as for the attention forward; tau_iters counts the sweeps that
+ * evaluated f (the row-max and histogram passes are not counted).
+ *  s          [rows, n] in_dtype, dense row-major        (read)
+ *  p          [rows, n] out_dtype                        (written)
+ *  tau        float32 [rows]                             (written)
+ *  tau_iters  uint8 [rows] or NULL                       (written if non-NULL)
+ * Device pointers; s, p and tau 16-byte aligned.  1 <= n <= 2^20, rows >= 0.
+ * Errors: EA_ERR_NULL, EA_ERR_SHAPE, EA_ERR_DTYPE, EA_ERR_ALPHA, EA_ERR_ALIGN,
+ * EA_ERR_UNSUPPORTED (tau_mode, max_iters, tol) before anything is enqueued;
+ * EA_ERR_LAUNCH if the launch fails.  Asynchronous on `stream`; allocates
+ * nothing. */
+typedef struct {
+  int64_t rows;         /* number of rows */
+  int32_t n;            /* scores per row */
+  int32_t in_dtype;     /* EA_F32 | EA_BF16: s */
+  int32_t out_dtype;    /* EA_F32 | EA_BF16: p */
+  int32_t tau_mode;     /* EA_TAU_* */
+  int32_t max_iters;    /* 0 = default (12, or 40 for BISECT) */
+  float   tol;          /* stop when |f(tau)| <= tol; 0 = default 1e-6 */
+} ea_rows_desc;
+
+int entmax_rows(const void* s, float alpha, void* p, float* tau, uint8_t* tau_iters,
+                const ea_rows_desc* desc, void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* entmax_attn_strerror(int status);

@@ -165,6 +165,34 @@ def _workers(n):
     return n if n else len(os.sched_getaffinity(0))
 
 
+def forward_rows(qh, kh, vh, alpha: float, causal: bool, i0: int, i1: int):
+    """One head (2-D arrays [N, d]): (out, tau) of query rows i0 .. i1-1 in
+    float64.  attention_forward is this function applied block by block."""
+    x = scores(np.asarray(qh[i0:i1], np.float64), np.asarray(kh, np.float64), alpha, causal, i0)
+    t = tau_exact(x, alpha)
+    p = entmax_probs(x, t, alpha)
+    return p @ np.asarray(vh, np.float64), t, p
+
+
+def backward_rows(qh, kh, vh, doh, tau_rows, alpha: float, causal: bool, i0: int, i1: int):
+    """One head: the gradient terms contributed by query rows i0 .. i1-1,
+    (dq[i0:i1], dk_part, dv_part) with dk_part, dv_part of shape [N, d].
+    dq rows are complete; dK and dV are the sums of these parts over all row
+    blocks (attention_backward is exactly that sum), so for causal attention
+    the key rows j >= i0 of the last block's parts are already complete."""
+    qh, kh, vh, doh = (np.asarray(a, np.float64) for a in (qh, kh, vh, doh))
+    beta = beta_of(alpha)
+    rs = 1.0 / np.sqrt(qh.shape[-1])
+    x = scores(qh[i0:i1], kh, alpha, causal, i0)
+    t = np.maximum(x - np.asarray(tau_rows, np.float64)[:, None], 0.0)
+    p = t ** beta
+    u = np.where(t > 0.0, t ** (beta - 1.0), 0.0)
+    dp = doh[i0:i1] @ vh.T
+    delta = np.sum(u * dp, axis=-1) / np.sum(u, axis=-1)
+    ds = u * (dp - delta[:, None])
+    return (ds @ kh) * rs, (ds.T @ qh[i0:i1]) * rs, p.T @ doh[i0:i1]
+
+
 def attention_forward(q, k, v, alpha: float, causal: bool, return_probs: bool = False,
                       workers: int = 0):
     """Forward: returns (out, tau[, P]) in float64 with the leading shape of q.
@@ -183,11 +211,9 @@ def attention_forward(q, k, v, alpha: float, causal: bool, return_probs: bool = 
     def block(job):
         h, i0 = job
         i1 = min(n, i0 + ROW_BLOCK)
-        x = scores(qh[h, i0:i1], kh[h], alpha, causal, i0)
-        t = tau_exact(x, alpha)
-        p = entmax_probs(x, t, alpha)
+        o, t, p = forward_rows(qh[h], kh[h], vh[h], alpha, causal, i0, i1)
         tau[h, i0:i1] = t
-        out[h, i0:i1] = p @ vh[h]
+        out[h, i0:i1] = o
         if probs is not None:
             probs[h, i0:i1] = p
 
@@ -212,8 +238,6 @@ def attention_backward(q, k, v, dout, alpha: float, causal: bool, tau=None, work
     if tau is None:
         tau = attention_forward(q, k, v, alpha, causal, workers=workers)[1]
     tauh = np.asarray(tau, dtype=np.float64).reshape(nh, n)
-    beta = beta_of(alpha)
-    rs = 1.0 / np.sqrt(d)
     dq = np.zeros_like(qh)
     dk = np.zeros((nh,) + kh.shape[1:])
     dv = np.zeros((nh,) + vh.shape[1:])
@@ -221,16 +245,10 @@ def attention_backward(q, k, v, dout, alpha: float, causal: bool, tau=None, work
     def head(h):
         for i0 in range(0, n, ROW_BLOCK):
             i1 = min(n, i0 + ROW_BLOCK)
-            x = scores(qh[h, i0:i1], kh[h], alpha, causal, i0)
-            t = np.maximum(x - tauh[h, i0:i1, None], 0.0)
-            p = t ** beta
-            u = np.where(t > 0.0, t ** (beta - 1.0), 0.0)
-            dp = doh[h, i0:i1] @ vh[h].T
-            delta = np.sum(u * dp, axis=-1) / np.sum(u, axis=-1)
-            ds = u * (dp - delta[:, None])
-            dq[h, i0:i1] = (ds @ kh[h]) * rs
-            dk[h] += (ds.T @ qh[h, i0:i1]) * rs
-            dv[h] += p.T @ doh[h, i0:i1]
+            gq, gk, gv = backward_rows(qh[h], kh[h], vh[h], doh[h], tauh[h, i0:i1], alpha, causal, i0, i1)
+            dq[h, i0:i1] = gq
+            dk[h] += gk
+            dv[h] += gv
 
     with ThreadPoolExecutor(_workers(workers)) as ex:
         list(ex.map(head, range(nh)))

@@ -1,5 +1,5 @@
 """C ABI checks that need no GPU: the library loads, exports every function
-the header declares, plans workspace without N^2 terms, and rejects invalid
+the header declares, plans a workspace the size of the block mask, and rejects invalid
 arguments before touching the device."""
 import ctypes
 import os
@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "entmax_attn.h")
 
 def header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(entmax_attn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:size_t|int|const char\*)\s+(entmax_\w+)\s*\(", text, re.M)))
 
 
 def test_library_exports_every_declared_function():
@@ -40,27 +40,57 @@ def test_header_constants_match_binding():
 def test_desc_struct_layout():
     # int32 x 9 + float + pointer, natural alignment
     assert ctypes.sizeof(Bd.EaDesc) == 48
+    # int64 + int32 x 5 + float
+    assert ctypes.sizeof(Bd.EaRowsDesc) == 32
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("rows", -1, -2), ("n", 0, -2), ("n", (1 << 20) + 1, -2), ("in_dtype", 3, -3), ("out_dtype", 9, -3),
+    ("tau_mode", 4, -8), ("max_iters", 300, -8), ("tol", 2.0, -8)])
+def test_rows_invalid_desc_rejected(field, value, status):
+    d = A.make_rows_desc(4, 100)
+    setattr(d, field, value)
+    lib = A.load_library()
+    assert lib.entmax_rows(None, 1.5, None, None, None, ctypes.byref(d), None) == status
+
+
+def test_rows_argument_checks():
+    lib = A.load_library()
+    d = A.make_rows_desc(4, 100)
+    assert lib.entmax_rows(None, 1.5, None, None, None, None, None) == -1        # no descriptor
+    assert lib.entmax_rows(None, 1.0, None, None, None, ctypes.byref(d), None) == -4   # alpha
+    assert lib.entmax_rows(None, 1.5, None, None, None, ctypes.byref(d), None) == -1   # null tensors
+    assert lib.entmax_rows(ctypes.c_void_p(16 * 3 + 4), 1.5, ctypes.c_void_p(64), ctypes.c_void_p(128), None,
+                           ctypes.byref(d), None) == -5                                   # misaligned s
+    empty = A.make_rows_desc(0, 100)
+    assert lib.entmax_rows(None, 1.5, None, None, None, ctypes.byref(empty), None) == 0  # nothing to do
 
 
 def _align(x):
     return (x + 255) // 256 * 256
 
 
-def test_workspace_is_rows_plus_tiles():
-    """Workspace = one float per row + one half per (row, 64-key tile), rows
-    padded to 32 tiles (+ the transposed copies for fp32 inputs): about a 128th
-    of an fp32 N^2 score matrix."""
-    for n in (1000, 4096, 16384):
+def test_workspace_is_rows_plus_mask_sized_codes():
+    """Workspace = one float per row + one byte per (32-query block, 64-key
+    tile), rows padded to 64 tiles (the size of the block mask), + the
+    transposed copies for fp32 inputs.  It grows like the block mask (about
+    N^2 / 2048 bytes per head), never like a score matrix."""
+    for n in (1000, 4096, 16384, 131072):
         bh = 16
-        nk = -(-n // 64)
+        nk, nq = -(-n // 64), -(-n // 32)
         d = A.make_desc(1, bh, n, 128)
         ws = A.entmax_attn_workspace_bytes(d)
-        assert ws == _align(bh * n * 4) + _align(bh * n * (-(-nk // 32) * 32) * 2)
-        assert ws * 120 < bh * n * n * 4 or n < 4096
+        codes = _align(bh * nq * (-(-nk // 64) * 64))
+        assert ws == _align(bh * n * 4) + codes
+        assert ws <= bh * n * 4 + bh * nq * (nk + 63) + 512
         f = A.make_desc(1, bh, n, 128, in_dtype=0)
         tr = _align(bh * 128 * nk * 64 * 4)
-        mt = _align(bh * nk * ((-(-n // 32) + 3) // 4 * 4))      # transposed block mask
+        mt = _align(bh * nk * ((nq + 3) // 4 * 4))      # transposed block mask
         assert A.entmax_attn_workspace_bytes(f) == max(tr + ws, 3 * tr + _align(bh * n * 4) + mt)
+    # the largest accepted length: one head at N = 2^20 needs the 512 MiB of
+    # its block mask plus 4 MiB of row maxima
+    big = A.entmax_attn_workspace_bytes(A.make_desc(1, 1, 1 << 20, 128))
+    assert big == (1 << 22) + (1 << 15) * (1 << 14)
     d = A.make_desc(2, 3, 1000, 64, out_dtype=1)
     assert A.entmax_attn_mask_dims(d) == (32, 16, 32, 64)
 

@@ -1,6 +1,9 @@
 """GPU parity at the reference workloads' full sizes, in the configuration the
 benchmark times (all heads in one call, bf16 in and out), checked against the
-float64 oracle on sampled heads computed one by one at full sequence length."""
+float64 oracle on sampled heads computed one by one at full sequence length.
+Extra cases: the headline workload with fp32 outputs (so the absolute bound
+applies to unrounded outputs), and the long-context workload in the two other
+tau modes (Halley-bisection from the bracket's lower end, plain bisection)."""
 import sys
 
 import numpy as np
@@ -14,32 +17,37 @@ from tests import parity as PT
 
 pytestmark = pytest.mark.gpu
 
+# (workload, overrides, output dtype ("in": same as the inputs), tau mode)
 CASES = [
-    ("small_f32", {}),
-    ("iid_causal_4k", {"scale": 1.0}),
-    ("iid_causal_4k", {"scale": 2.0}),
-    ("iid_causal_4k", {"scale": 4.0}),
-    ("planted_16k", {}),
-    ("encoder_8k", {"alpha": 1.25}),
-    ("encoder_8k", {"alpha": 1.5}),
-    ("encoder_8k", {"alpha": 2.0}),
-    ("planted_32k", {}),
+    ("small_f32", {}, "in", "hist"),
+    ("iid_causal_4k", {"scale": 1.0}, "in", "hist"),
+    ("iid_causal_4k", {"scale": 2.0}, "in", "hist"),
+    ("iid_causal_4k", {"scale": 4.0}, "in", "hist"),
+    ("planted_16k", {}, "in", "hist"),
+    ("planted_16k", {}, "f32", "hist"),
+    ("encoder_8k", {"alpha": 1.25}, "in", "hist"),
+    ("encoder_8k", {"alpha": 1.5}, "in", "hist"),
+    ("encoder_8k", {"alpha": 2.0}, "in", "hist"),
+    ("planted_32k", {}, "in", "hist"),
+    ("planted_32k", {}, "in", "halley"),
+    ("planted_32k", {}, "in", "bisect"),
 ]
 
 
 def _id(case):
-    name, kw = case
-    return name + "".join(f"-{k}{v}" for k, v in kw.items())
+    name, kw, out, mode = case
+    return name + "".join(f"-{k}{v}" for k, v in kw.items()) + ("" if out == "in" else f"-out{out}") + \
+        ("" if mode == "hist" else f"-{mode}")
 
 
 @pytest.mark.parametrize("case", CASES, ids=[_id(c) for c in CASES])
 def test_full_size_sampled_heads(case):
-    name, kw = case
+    name, kw, out_kind, mode = case
     w = G.workload(name, **kw)
-    print(f"\n[full-size] {_id(case)}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}", flush=True)
+    print(f"\n[full-size] {_id(case)}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} tau={mode}", flush=True)
     x = G.make_inputs(w)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    bufs = A.Buffers(w.B, w.H, w.N, w.d, dt, dt, "hist")
+    bufs = A.Buffers(w.B, w.H, w.N, w.d, dt, torch.float32 if out_kind == "f32" else dt, mode)
     dev = [torch.from_numpy(x[n]).to(dt).cuda() for n in ("q", "k", "v", "dout")]
     bufs.forward(dev[0], dev[1], dev[2], w.alpha, w.causal)
     if w.backward:

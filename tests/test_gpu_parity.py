@@ -218,3 +218,39 @@ def test_f32_d128():
     w = G.workload("planted_16k", H=1, N=300, dtype="f32")
     x = G.make_inputs(w)
     check_all(w, x, run(w, x))
+
+
+def test_tied_keys_beyond_65536():
+    """N = 70000 with the first 68000 keys identical (one centroid, queries
+    aligned with it, so the tied score is every row's maximum): rows past
+    65536 put more than 65536 tied scores into the top histogram bin, where a
+    2^-24 fixed point would overflow the packed moments.  Forward and
+    backward run in full; the first 256 and the last 512 query rows are
+    checked against the oracle (tau, support, mask rows, out, dq), and so are
+    dK / dV of the last 512 keys, which only those rows reach (causal)."""
+    w = G.workload("iid_causal_4k", B=1, H=1, N=70000, d=64, gen="tied", ties=68000, strength=2.0)
+    print(f"\n[ties] B={w.B} H={w.H} N={w.N} d={w.d} ties={w.ties}", flush=True)
+    x = G.make_inputs(w)
+    res = run(w, x)
+    q, k, v, do = (x[n][0, 0].astype(np.float64) for n in ("q", "k", "v", "dout"))
+    tol = PT.out_tol(w.dtype)
+    for i0, i1 in ((0, 256), (w.N - 512, w.N)):
+        out_ref, tau_ref, _ = O.forward_rows(q, k, v, w.alpha, w.causal, i0, i1)
+        tau = res["tau"][0, 0, i0:i1]
+        PT.check_tau(tau, tau_ref)
+        PT.check_close(f"out[{i0}:{i1}]", res["out"][0, 0, i0:i1], out_ref, tol)
+        xs = O.scores(q[i0:i1], k, w.alpha, w.causal, i0)
+        diff = (xs > tau[:, None]) != (xs > tau_ref[:, None])
+        assert np.all(np.abs(xs - tau_ref[:, None])[diff] <= PT.SUPPORT_BAND), "support differs"
+        # mask rows of the sampled 32-query blocks cover every active tile
+        need = (xs - tau_ref[:, None] > PT.SUPPORT_BAND)
+        pad = np.zeros((i1 - i0, -(-w.N // 64) * 64 - w.N), bool)
+        need = np.concatenate([need, pad], 1).reshape((i1 - i0) // 32, 32, -1, 64).any(axis=(1, 3))
+        got = res["mask"][0, 0, i0 // 32:i1 // 32].astype(bool)
+        assert not np.any(need & ~got), "block mask misses active tiles"
+        gq, gk, gv = O.backward_rows(q, k, v, do, tau_ref, w.alpha, w.causal, i0, i1)
+        PT.check_close(f"dq[{i0}:{i1}]", res["dq"][0, 0, i0:i1], gq, tol)
+        if i1 == w.N:
+            PT.check_close("dk[last 512]", res["dk"][0, 0, i0:], gk[i0:], tol)
+            PT.check_close("dv[last 512]", res["dv"][0, 0, i0:], gv[i0:], tol)
+    assert np.all(res["iters"] >= 1)

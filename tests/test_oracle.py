@@ -317,3 +317,50 @@ def test_planted_mutation_is_caught():
     dq_bad = mutated(q, k, v, do, 1.5, False)
     dq_good = orig(q, k, v, do, 1.5, False)[0]
     assert np.abs(dq_bad - dq_good).max() > 1e-3
+
+
+# ------------------------------------------- f and element sparsity pins ---
+
+FSP = os.path.join(os.path.dirname(__file__), "golden", "f_and_sparsity.json")
+
+
+def test_entmax_f_hand_values():
+    """f at non-root points, solved by hand (tests/golden/f_and_sparsity.json):
+    a dropped '- 1', a wrong exponent or a missing (alpha - 1) factor fails."""
+    for c in json.load(open(FSP))["f_values"]:
+        x = (c["alpha"] - 1.0) * np.asarray([c["s"]], dtype=np.float64)
+        f = O.entmax_f(x, np.asarray([c["tau"]]), c["alpha"])
+        assert f[0] == pytest.approx(_eval(c["f"]), abs=1e-12), c
+
+
+def test_entmax_f_vanishes_at_golden_tau():
+    """At the hand-derived tau of every closed-form example, f = 0."""
+    for c in json.load(open(GOLDEN))["cases"]:
+        x = (c["alpha"] - 1.0) * np.asarray([c["s"]], dtype=np.float64)
+        f = O.entmax_f(x, np.asarray([_eval(c["tau"])]), c["alpha"])
+        assert abs(f[0]) <= 1e-12, c["name"]
+
+
+@pytest.mark.parametrize("alpha", [1.25, 1.5, 1.75, 2.0])
+def test_entmax_f_bracket_signs(alpha):
+    """f(max x - 1) >= 0 >= f(max x - n^(1-alpha)) (proved from the definition:
+    the top term alone is 1 at the lower end, every term is at most 1/n at the
+    upper end), and f decreases strictly between them."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 37)) * rng.uniform(0.1, 5.0, (64, 1))
+    lo, hi = O.tau_bracket(x, alpha)
+    assert np.all(O.entmax_f(x, lo, alpha) >= 0.0)
+    assert np.all(O.entmax_f(x, hi, alpha) <= 1e-15)
+    mid = 0.5 * (lo + hi)
+    assert np.all(O.entmax_f(x, lo, alpha) > O.entmax_f(x, mid, alpha))
+    assert np.all(O.entmax_f(x, mid, alpha) > O.entmax_f(x, hi, alpha))
+
+
+def test_element_sparsity_hand_counts():
+    """Hand counts of zero-probability visible entries on tiny d = 1 cases,
+    with entries exactly on the threshold (which count as zeros: p = 0 there),
+    causal and not, one and two heads."""
+    for c in json.load(open(FSP))["element_sparsity"]:
+        q, k, tau = (np.asarray(c[n], dtype=np.float64) for n in ("q", "k", "tau"))
+        got = O.element_sparsity(q, k, c["alpha"], c["causal"], tau)
+        assert got == pytest.approx(_eval(c["sparsity"]), abs=1e-15), c
