@@ -63,6 +63,11 @@ constexpr int kBQW = kBQ * kWaves;    // queries per workgroup (forward, dQ)
 constexpr int kBK = 64;               // keys per tile = mask column granularity
 constexpr int kThreads = kWave * kWaves;
 
+// Block mask byte of a (32-query, 64-key) tile: bit 0 = the tile holds a
+// nonzero probability; bits 1 and 2 = keys 0-31 / 32-63 of the tile do (the
+// 32x32 micro-tiles that P V and the backward skip on their own).
+__host__ __device__ constexpr uint32_t half_bits(uint32_t m) { return m ? ((m >> 1) & 3u) : 0u; }
+
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -549,17 +554,17 @@ struct ColStage {
 };
 
 // Compacts tiles base..base+len-1 whose wave bits (pred(w, t) for the four
-// waves) are not all zero into list[] / wbits[]; returns the count.  Every
-// thread of the workgroup must call it.  `flags` holds len bytes of scratch.
-template <typename Pred>
+// waves, BITS bits each at bit BITS * w) are not all zero into list[] /
+// wbits[]; returns the count.  Every thread of the workgroup must call it.
+// `flags` holds len bytes of scratch.
+template <int BITS = 1, typename Pred>
 __device__ __forceinline__ int build_list(int base, int len, Pred pred, short* list, uint8_t* wbits,
                                           uint8_t* flags, int* counter) {
   for (int i = threadIdx.x; i < len; i += kThreads) {
-    uint8_t b = 0;
+    uint32_t b = 0;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww)
-      if (pred(ww, base + i)) b |= (uint8_t)(1u << ww);
-    flags[i] = b;
+    for (int ww = 0; ww < kWaves; ++ww) b |= ((uint32_t)pred(ww, base + i) & ((1u << BITS) - 1u)) << (BITS * ww);
+    flags[i] = (uint8_t)b;
   }
   __syncthreads();
   if (threadIdx.x < kWave) {
@@ -942,8 +947,14 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const char* kl, 
   const int h = lane >> 5, c32 = lane & 31;
   f32x16 acc[2];
   tile_scores<E, D>(acc, kl, KS, qf, lane, lim, std::integral_constant<bool, M>{});
+  bool live[2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb) {
+    float mx = acc[kb][0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmax_nan(mx, acc[kb][j]);
+    // the 32x32 micro-tile holds a nonzero probability for some query
+    live[kb] = __ballot(fmaf(mx, P.scale, -tau) > 0.0f) != 0ull;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
@@ -951,8 +962,10 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const char* kl, 
       Ent<AK>::pu(t, P.beta, p, u);
       acc[kb][j] = p;
     }
+  }
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb) {
+    if (!live[kb]) continue;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       Frag<E> pf;
@@ -970,6 +983,7 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const char* kl, 
         mma(oacc[db], vf, pf);
       }
     }
+  }
 }
 
 // Writes a wave's O accumulators for query iq (fp32 or bf16 out).
@@ -1364,7 +1378,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   // ---- refinement sweeps (Halley-bisection or bisection) over candidate tiles
   uint8_t* mrow = mask_out + ((size_t)bh * P.n_q32 + (size_t)r32) * P.n_kt;
   if (wave_rows) {
-    for (int kt = lane; kt < P.n_kt; kt += kWave) mrow[kt] = (dense && kt < kt_end_w) ? 1 : 0;
+    for (int kt = lane; kt < P.n_kt; kt += kWave) mrow[kt] = (dense && kt < kt_end_w) ? 7 : 0;
   }
   if constexpr (kFusePV) {
     // the same mask as bits in LDS for the P V epilogue
@@ -1411,17 +1425,23 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
       auto body = [&](auto masked) {
         f32x16 acc[2];
         tile_scores<E, D>(acc, kl, KS, qf, lane, row_limit(kt * kBK, iq, N, P.causal, h), masked);
-        const float before = Ent<AK>::count(F0, F1, F2, cnt);
+        float cnt_at[3];
+        cnt_at[0] = Ent<AK>::count(F0, F1, F2, cnt);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int j = 0; j < 16; ++j) {
             const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
             Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
           }
+          cnt_at[kb + 1] = Ent<AK>::count(F0, F1, F2, cnt);
+        }
         if (!dense) {
-          const bool any = __ballot(Ent<AK>::count(F0, F1, F2, cnt) > before) != 0ull;
-          if (lane == (kt & (kWave - 1))) mrow[kt] = any ? 1 : 0;   // same lane as the zero fill
+          const bool any0 = __ballot(cnt_at[1] > cnt_at[0]) != 0ull;
+          const bool any1 = __ballot(cnt_at[2] > cnt_at[1]) != 0ull;
+          const bool any = any0 || any1;
+          if (lane == (kt & (kWave - 1)))   // same lane as the zero fill
+            mrow[kt] = any ? (uint8_t)(1u | (any0 ? 2u : 0u) | (any1 ? 4u : 0u)) : 0;
           if (kFusePV && any && lane == 0) atomicOr(&mbits[w * n_words + (kt >> 5)], 1u << (kt & 31));
           // does the tile hold a score above some row's lower bracket end?
           float mx = fmax_nan(acc[0][0], acc[1][0]);
@@ -1718,9 +1738,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   float num = 0.0f, den = 0.0f, dlt = 0.0f;
 
   const size_t mrow0 = (size_t)bh * P.n_q32 + (size_t)qtile * kWaves;
-  auto active = [&](int ww, int kt) -> bool {
-    return (qtile * kWaves + ww) < P.n_q32 && mask[(mrow0 + ww) * P.n_kt + kt] != 0;
+  // the wave's mask byte of tile kt (0 past the last query block)
+  auto mbyte = [&](int ww, int kt) -> uint32_t {
+    return (qtile * kWaves + ww) < P.n_q32 ? (uint32_t)mask[(mrow0 + ww) * P.n_kt + kt] : 0u;
   };
+  // two bits per wave: which 32-key halves of the tile hold a probability
+  auto halves = [&](int ww, int kt) -> uint32_t { return half_bits(mbyte(ww, kt)); };
   RowTiles<E, D, kBK> sk(K + hoff, N, w, lane), sv(V + hoff, N, w, lane);
   ColStage<E, D, kBK> st;
   // With one list chunk (n_kt <= kChunk) both passes walk the same list: it
@@ -1756,7 +1779,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     const bool hand_over = single && pass == 0;      // fetch pass 2's first tile at the end
     for (int base = 0; base < P.n_kt; base += kChunk) {
       const int n = reuse ? n_first
-                          : build_list(base, min(kChunk, P.n_kt - base), active, list, wbits, flags, counter);
+                          : build_list<2>(base, min(kChunk, P.n_kt - base), halves, list, wbits, flags, counter);
       if (hand_over) n_first = n;
       const int s0 = reuse ? n_first : 0;            // step index of this pass's first tile
       if (n > 0 && !reuse) {
@@ -1772,7 +1795,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
           load(pass, (base + list[i + 1]) * kBK, nb);
         else if (hand_over)
           load(1, (base + list[0]) * kBK, nb);
-        if ((wbits[i] >> w) & 1) {
+        const uint32_t hv = (wbits[i] >> (2 * w)) & 3u;   // this wave's live halves
+        if (hv) {
           const int buf = NB == 2 ? ((s0 + i) & 1) : 0;
           const char* kl = kbuf + buf * kBK * KS;
           auto body = [&](auto masked) {
@@ -1784,6 +1808,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
             const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
+              if (!((hv >> kb) & 1u)) continue;   // no probability in this 32x32 micro-tile
               f32x16 sacc, pacc;
               scores_T_half2<E, D>(sacc, pacc, kl, vl, KS, kb, qf, of, lane);
               if constexpr (decltype(masked)::value) mask_half_rows_above(sacc, kb, lim);
@@ -1853,8 +1878,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     for (int kt = threadIdx.x; kt < P.n_kt; kt += kThreads) {
       uint32_t word = 0;
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww)
-        if (active(ww, kt)) word |= 1u << (8 * ww);
+      for (int ww = 0; ww < kWaves; ++ww) word |= mbyte(ww, kt) << (8 * ww);
       *reinterpret_cast<uint32_t*>(maskT + ((size_t)bh * P.n_kt + kt) * np + qtile * kWaves) = word;
     }
   }
@@ -1946,12 +1970,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   }
   const int ktA = (ktile * 128) / kBK, ktB = ktA + 1;
   const int np = (P.n_q32 + 3) & ~3;
-  // waves 0, 1 cover key tile A (64 keys), waves 2, 3 key tile B; the
-  // transposed mask gives each key tile's query rows contiguously
+  // waves 0, 1 cover the two 32-key halves of key tile A, waves 2, 3 those of
+  // key tile B: a wave's work is one 32x32 micro-tile per query block, live
+  // when the mask byte's bit for its half is set.  The transposed mask gives
+  // each key tile's query rows contiguously.
   auto active = [&](int ww, int r) -> bool {
     const int kt = ww < 2 ? ktA : ktB;
     if (kt >= P.n_kt || (ktile * 128 + 32 * ww) >= N) return false;
-    return maskT[((size_t)bh * P.n_kt + kt) * np + r] != 0;
+    return (half_bits(maskT[((size_t)bh * P.n_kt + kt) * np + r]) >> (ww & 1)) & 1u;
   };
 
   RowTiles<E, D, kBQ> sq(Q + hoff, N, w, lane), so(dO + hoff, N, w, lane);

@@ -72,6 +72,17 @@ def visible_fraction_tiles(n, bm, bn, causal):
     return vis
 
 
+def micro_sparsity(mask: np.ndarray, n: int, causal: bool):
+    """Sparsity over causally visible 32x32 micro-tiles, from the half bits of
+    the mask bytes (bit 1: keys 0-31 of the 64-key tile, bit 2: keys 32-63)."""
+    nh, nq, nk = mask.shape
+    m = mask.astype(np.uint8)
+    halves = np.stack([(m >> 1) & 1, (m >> 2) & 1], axis=-1).astype(bool) & (m != 0)[..., None]
+    halves = halves.reshape(nh, nq, 2 * nk)[:, :, :-(-n // 32)]
+    vis = visible_fraction_tiles(n, 32, 32, causal)
+    return 1.0 - (halves & vis[None]).sum() / (vis.sum() * nh)
+
+
 def block_sparsity(mask: np.ndarray, n: int, causal: bool, group: int):
     """Sparsity over causally visible tiles after OR-ing `group` mask rows."""
     nh, nq, nk = mask.shape
@@ -239,6 +250,7 @@ class Runner:
         iters = self.bufs.iters.cpu().numpy()
         ms = (t1 - t0) / steps * 1e3
         return {"ms_per_step": ms, "tflops": dense_equiv_flops(w) / (ms * 1e-3) / 1e12,
+                "block_sparsity_32x32": micro_sparsity(mask, w.N, w.causal),
                 "block_sparsity_32x64": block_sparsity(mask, w.N, w.causal, 1),
                 "block_sparsity_128x64": block_sparsity(mask, w.N, w.causal, 4),
                 "tau_iters_mean": float(iters.mean()), "tau_iters_max": int(iters.max()),
@@ -382,6 +394,7 @@ def main():
         "config": {
             "workload": describe(w),
             "tau_mode": args.tau_mode,
+            "block_sparsity_32x32": head["block_sparsity_32x32"],
             "block_sparsity_32x64": head["block_sparsity_32x64"],
             "block_sparsity_128x64": head["block_sparsity_128x64"],
             "element_sparsity": elem_sp,
@@ -398,7 +411,7 @@ def main():
         # ---- throughput vs block sparsity: the same generator at weaker query
         # strengths (5 timed steps each after 2 warm-up steps)
         sweep = [dict(strength=w.strength, **{k_: head[k_] for k_ in (
-            "ms_per_step", "tflops", "block_sparsity_32x64", "block_sparsity_128x64",
+            "ms_per_step", "tflops", "block_sparsity_32x32", "block_sparsity_32x64", "block_sparsity_128x64",
             "tau_iters_mean", "tau_iters_max", "stage_ms")}, element_sparsity=elem_sp)]
         for a in (0.5, 0.4, 0.3):
             wa = w.with_(strength=a)

@@ -111,16 +111,30 @@ typedef struct {
 size_t entmax_attn_workspace_bytes(const ea_desc* desc);
 
 /* Shape of block_mask: [B, H, n_qt, n_kt] bytes with n_qt = ceil(N/bm),
- * n_kt = ceil(N/bn).  Any output pointer may be NULL.  Returns a status. */
+ * n_kt = ceil(N/bn), bm = 32 queries, bn = 64 keys: the tiles whose all-zero
+ * probabilities the output pass and the backward skip ("AdaSplash: Adaptive
+ * Sparse Flash Attention", "Exploiting Sparsity").  Any output pointer may be
+ * NULL.  Returns a status. */
 int entmax_attn_mask_dims(const ea_desc* desc, int* n_qt, int* n_kt, int* bm, int* bn);
 
-/* Forward pass.
+/* Forward pass: tau, the block mask and o = P V, with S and P never written
+ * to memory ("AdaSplash: Adaptive Sparse Flash Attention", "AdaSplash: Fused
+ * GPU Kernel for Attention"; tau by Halley-bisection, "Accelerated
+ * Alpha-Entmax Transformation", started from a per-row histogram in
+ * EA_TAU_HIST_HALLEY mode, "AdaSplash-2: The Transformer Revolution We Didn't
+ * See Coming", "Sparse Attention Makes Waves").
  *  q, k, v     [B,H,N,d] in_dtype                     (read)
  *  out         [B,H,N,d] out_dtype                    (written)
  *  tau         float32 [B,H,N]                        (written)
- *  block_mask  uint8 [B,H,n_qt,n_kt] (mask_dims)      (written): 1 where the
- *              tile holds a visible entry with x > tau, 0 otherwise (a tile
- *              marked 1 may still be all-zero only within float32 rounding).
+ *  block_mask  uint8 [B,H,n_qt,n_kt] (mask_dims)      (written): nonzero where
+ *              the tile holds a visible entry with x > tau, 0 otherwise (a
+ *              tile marked nonzero may still be all-zero only within float32
+ *              rounding).  Bit 0 marks the tile; bits 1 and 2 mark the 32x32
+ *              micro-tiles (keys 0-31, 32-63 of the tile) that hold such an
+ *              entry, which P V and the backward skip on their own ("AdaSplash:
+ *              Adaptive Sparse Flash Attention", "Exploiting Sparsity": zero
+ *              blocks skipped at micro-tile granularity).  With
+ *              EA_FLAG_FORCE_DENSE every visible tile reads 7.
  *  tau_iters   uint8 [B,H,N] or NULL                  (written if non-NULL):
  *              refinement sweeps that evaluated f(tau) for the row (the
  *              row-max and histogram sweeps are not counted).
@@ -131,9 +145,14 @@ int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, in
                     void* out, float* tau, uint8_t* block_mask, uint8_t* tau_iters,
                     const ea_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward pass.  tau and block_mask must come from entmax_attn_fwd on the
+/* Backward pass over the tiles the forward found nonzero ("AdaSplash:
+ * Adaptive Sparse Flash Attention", "Backward Pass": skipping all-zero tiles
+ * makes the backward sub-quadratic; the gradient formula above is derived
+ * from the definition of tau).  tau and block_mask must come from entmax_attn_fwd on the
  * same q, k, v, alpha, causal and desc (they are the only forward state the
- * backward needs; delta_i = sum_j u_ij dP_ij / sum_j u_ij is recomputed).
+ * backward needs; delta_i = sum_j u_ij dP_ij / sum_j u_ij is recomputed, so
+ * no other forward-to-backward buffer exists).  Skips the tiles and 32x32
+ * micro-tiles block_mask marks empty.
  *  dout        [B,H,N,d] in_dtype                     (read)
  *  dq, dk, dv  [B,H,N,d] out_dtype                    (written)
  */

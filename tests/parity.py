@@ -106,6 +106,25 @@ def check_mask(mask_gpu, margins, band=SUPPORT_BAND):
     return int(fp.sum()), int(need.sum())
 
 
+def micro_mask(mask_gpu, n):
+    """32x32 micro-tile bits from the mask bytes: bit 1 covers keys 0-31 of a
+    64-key tile, bit 2 keys 32-63.  Shape [..., n_q32, ceil(n / 32)]."""
+    m = np.asarray(mask_gpu).astype(np.uint8)
+    halves = np.stack([(m >> 1) & 1, (m >> 2) & 1], axis=-1).astype(bool)
+    halves &= (m != 0)[..., None]
+    return halves.reshape(m.shape[:-1] + (2 * m.shape[-1],))[..., :-(-n // 32)]
+
+
+def check_micro_mask(mask_gpu, margins32, n, band=SUPPORT_BAND):
+    """Every 32x32 micro-tile the oracle finds active beyond the band has its
+    bit set; returns (false-positive micro-tiles, active micro-tiles)."""
+    mm = micro_mask(mask_gpu, n)
+    need = margins32 > band
+    missing = need & ~mm
+    assert not missing.any(), f"micro-tile bits miss {missing.sum()} active 32x32 tiles"
+    return int((mm & ~(margins32 > -band)).sum()), int(need.sum())
+
+
 def visible_tiles(n, bm, bn, causal):
     nq, nk = -(-n // bm), -(-n // bn)
     vis = np.ones((nq, nk), dtype=bool)

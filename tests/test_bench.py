@@ -55,3 +55,14 @@ def test_cpu_baseline_sample_is_bounded():
     assert "on 2 of 3 heads" in capped["sample"]
     every = bench.cpu_baseline(w, x, max_heads=10, min_seconds=1e9)
     assert "on 3 of 3 heads" in every["sample"]
+
+
+def test_micro_sparsity_reads_half_bits():
+    n = 128                      # 4 query rows of 32, 2 key tiles of 64 = 4 micro columns
+    m = np.zeros((1, 4, 2), np.uint8)
+    m[0, 0, 0] = 1 | 2           # row 0: keys 0-31 only
+    m[0, 3, 1] = 1 | 2 | 4       # row 3: keys 64-127
+    vis = bench.visible_fraction_tiles(n, 32, 32, True)
+    assert vis.sum() == 1 + 2 + 3 + 4
+    assert np.isclose(bench.micro_sparsity(m, n, True), 1 - 3 / 10)
+    assert np.isclose(bench.block_sparsity(m, n, True, 1), 1 - 2 / bench.visible_fraction_tiles(n, 32, 64, True).sum())

@@ -67,7 +67,10 @@ def test_full_size_sampled_heads(case):
         PT.check_support(q, k, w.alpha, w.causal, tau, tau_ref)
         margins = O.tile_margins(q, k, w.alpha, w.causal, tau_ref, 32, 64)
         fp, act = PT.check_mask(flat(bufs.mask)[sl].cpu().numpy(), margins)
-        print(f"  head {hh}: active tiles {act}, false-positive tiles {fp}", flush=True)
+        m32 = O.tile_margins(q, k, w.alpha, w.causal, tau_ref, 32, 32)
+        fp32, act32 = PT.check_micro_mask(flat(bufs.mask)[sl].cpu().numpy(), m32, w.N)
+        print(f"  head {hh}: active tiles {act} (32x64), {act32} (32x32); false positives {fp}, {fp32}",
+              flush=True)
         if w.backward:
             dq, dk, dv = O.attention_backward(q, k, v, do, w.alpha, w.causal, tau=tau_ref)
             PT.check_close(f"dq[h{hh}]", flat(bufs.dq)[sl].float().cpu().numpy(), dq, tol)

@@ -41,6 +41,7 @@ def check_all(w, x, res, backward=True):
     PT.check_support(q, k, w.alpha, w.causal, res["tau"], tau_ref)
     margins = O.tile_margins(q, k, w.alpha, w.causal, tau_ref, MASK_BM, MASK_BN)
     PT.check_mask(res["mask"], margins)
+    PT.check_micro_mask(res["mask"], O.tile_margins(q, k, w.alpha, w.causal, tau_ref, 32, 32), w.N)
     # invisible tiles are never active
     vis = PT.visible_tiles(w.N, MASK_BM, MASK_BN, w.causal)
     assert not np.any(res["mask"].astype(bool) & ~vis)
