@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     entmax_attention,
     entmax_attn_bwd,
     entmax_attn_fwd,
+    entmax_attn_fwd_static,
     entmax_attn_mask_dims,
     entmax_attn_workspace_bytes,
     entmax_rows,

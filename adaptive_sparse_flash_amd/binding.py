@@ -26,6 +26,7 @@ EXPORTED = (
     "entmax_attn_workspace_bytes",
     "entmax_attn_mask_dims",
     "entmax_attn_fwd",
+    "entmax_attn_fwd_static",
     "entmax_attn_bwd",
     "entmax_rows",
     "entmax_attn_strerror",
@@ -77,6 +78,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.entmax_attn_mask_dims.restype = i32
     lib.entmax_attn_fwd.argtypes = [vp, vp, vp, f32, i32, vp, vp, vp, vp, dp, vp, sz, vp]
     lib.entmax_attn_fwd.restype = i32
+    lib.entmax_attn_fwd_static.argtypes = [vp, vp, vp, f32, i32, vp, vp, vp, vp, dp, vp]
+    lib.entmax_attn_fwd_static.restype = i32
     lib.entmax_attn_bwd.argtypes = [vp, vp, vp, f32, i32, vp, vp, vp, vp, vp, vp, dp, vp, sz, vp]
     lib.entmax_attn_bwd.restype = i32
     lib.entmax_rows.argtypes = [vp, f32, vp, vp, vp, ctypes.POINTER(EaRowsDesc), vp]
@@ -172,6 +175,20 @@ def entmax_attn_fwd(q, k, v, alpha, causal, out, tau, block_mask, tau_iters, des
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     if st != EA_OK:
         raise EntmaxAttnError(st, "entmax_attn_fwd")
+
+
+def entmax_attn_fwd_static(q, k, v, alpha, causal, out, tau, block_mask, tau_iters, desc, stream=None) -> None:
+    """The forward on the library's fixed device scratch array (no workspace)."""
+    full, rows, mask = _sizes(desc)
+    ti, to = _TORCH_DTYPE.get(desc.in_dtype), _TORCH_DTYPE.get(desc.out_dtype)
+    _check_tensors(desc, "entmax_attn_fwd_static", q=(q, full, ti), k=(k, full, ti), v=(v, full, ti),
+                   out=(out, full, to), tau=(tau, rows, torch.float32),
+                   block_mask=(block_mask, mask, torch.uint8), tau_iters=(tau_iters, rows, torch.uint8))
+    st = load_library().entmax_attn_fwd_static(
+        _ptr(q), _ptr(k), _ptr(v), float(alpha), int(bool(causal)), _ptr(out), _ptr(tau),
+        _ptr(block_mask), _ptr(tau_iters), ctypes.byref(desc), _stream(stream))
+    if st != EA_OK:
+        raise EntmaxAttnError(st, "entmax_attn_fwd_static")
 
 
 def entmax_attn_bwd(q, k, v, alpha, causal, dout, tau, block_mask, dq, dk, dv, desc, ws,

@@ -50,6 +50,7 @@
 #include <float.h>
 
 #include <climits>
+#include <mutex>
 #include <type_traits>
 
 #include "entmax_attn.h"
@@ -2686,6 +2687,37 @@ int dispatch_rows_ak(float alpha, const ea_rows_desc* d, RowParams P, const void
   }
 }
 
+// ------------------------------------------------ no-allocation forward ---
+// entmax_attn_fwd_static runs the forward on a fixed-size file-scope device
+// array instead of a caller workspace.  Every GPU the library runs on holds
+// its own copy of the array until the process ends.  In host code the array's
+// name is not a device address: the address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that pointer is
+// passed to kernels.  Calls on one GPU share the array, so overlapping calls
+// there race; the forward writes every workspace byte it later reads, so
+// nothing needs clearing between calls.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return EA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return EA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return EA_OK;
+}
+
+// forward part of the workspace: [V^T] | row maxima | block codes
+size_t fwd_workspace_bytes(const Shape& s) { return transposed_bytes(s) + row_bytes(s) + blkcode_bytes(s); }
+
 #define EA_DISPATCH(FN, ...)                                                          \
   do {                                                                                \
     const int ak = alpha_kind(alpha);                                                 \
@@ -2759,6 +2791,28 @@ int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, in
         misaligned(ws))
       return EA_ERR_ALIGN;
     if (ws_bytes < workspace_bytes(s)) return EA_ERR_WORKSPACE;
+  }
+  Params P = make_params(desc, s, alpha, causal);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  EA_DISPATCH(launch_fwd, s, P, q, k, v, out, tau, block_mask, tau_iters, ws, hs,
+              StageTimer{desc->events, hs});
+}
+
+int entmax_attn_fwd_static(const void* q, const void* k, const void* v, float alpha, int causal, void* out,
+                           float* tau, uint8_t* block_mask, uint8_t* tau_iters, const ea_desc* desc,
+                           void* stream) {
+  Shape s;
+  int st = check_desc(desc, &s);
+  if (st != EA_OK) return st;
+  if ((st = check_alpha(alpha)) != EA_OK) return st;
+  if (causal != 0 && causal != 1) return EA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (s.N > 0) {
+    if (!q || !k || !v || !out || !tau || !block_mask) return EA_ERR_NULL;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(tau))
+      return EA_ERR_ALIGN;
+    if (fwd_workspace_bytes(s) > kStaticScratchBytes) return EA_ERR_WORKSPACE;
+    if ((st = static_scratch(&ws)) != EA_OK) return st;
   }
   Params P = make_params(desc, s, alpha, causal);
   hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -145,6 +145,21 @@ int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, in
                     void* out, float* tau, uint8_t* block_mask, uint8_t* tau_iters,
                     const ea_desc* desc, void* ws, size_t ws_bytes, void* stream);
 
+/* Forward pass without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as
+ * entmax_attn_fwd, minus ws / ws_bytes: the workspace is a fixed 32 MiB
+ * device array inside the library, one per GPU for the life of the process,
+ * and this call allocates nothing.  A desc whose forward workspace exceeds
+ * 32 MiB returns EA_ERR_WORKSPACE before anything is enqueued (about
+ * B*H*(4 N + N^2/2048) bytes for bf16 inputs: e.g. 16 heads at N = 32768 fit).
+ * All calls on one GPU share the array: calls that overlap on one GPU (other
+ * streams, other host threads) race.  entmax_attn_bwd still takes a caller
+ * workspace. */
+int entmax_attn_fwd_static(const void* q, const void* k, const void* v, float alpha, int causal,
+                           void* out, float* tau, uint8_t* block_mask, uint8_t* tau_iters,
+                           const ea_desc* desc, void* stream);
+
 /* Backward pass over the tiles the forward found nonzero ("AdaSplash:
  * Adaptive Sparse Flash Attention", "Backward Pass": skipping all-zero tiles
  * makes the backward sub-quadratic; the gradient formula above is derived
