@@ -40,6 +40,7 @@ class EaDesc(ctypes.Structure):
         ("tau_mode", ctypes.c_int32), ("max_iters", ctypes.c_int32),
         ("tol", ctypes.c_float), ("flags", ctypes.c_int32),
         ("events", ctypes.POINTER(ctypes.c_void_p)),
+        ("key_lens", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -104,11 +105,19 @@ def _dtype_code(dt: torch.dtype) -> int:
 
 
 def make_desc(B, H, N, d, in_dtype=torch.bfloat16, out_dtype=torch.float32, tau_mode="hist",
-              max_iters=0, tol=0.0, force_dense=False) -> EaDesc:
+              max_iters=0, tol=0.0, force_dense=False, key_lens=None) -> EaDesc:
+    """Descriptor; key_lens (B ints, or None) selects variable-length batches.
+    The host array it points to is kept alive by the descriptor."""
     mode = TAU_MODES[tau_mode] if isinstance(tau_mode, str) else int(tau_mode)
-    return EaDesc(B, H, N, d, _dtype_code(in_dtype) if isinstance(in_dtype, torch.dtype) else in_dtype,
+    desc = EaDesc(B, H, N, d, _dtype_code(in_dtype) if isinstance(in_dtype, torch.dtype) else in_dtype,
                   _dtype_code(out_dtype) if isinstance(out_dtype, torch.dtype) else out_dtype,
-                  mode, max_iters, tol, EA_FLAG_FORCE_DENSE if force_dense else 0, None)
+                  mode, max_iters, tol, EA_FLAG_FORCE_DENSE if force_dense else 0, None, None)
+    if key_lens is not None:
+        if len(key_lens) != B:
+            raise ValueError(f"key_lens has {len(key_lens)} entries, expected B = {B}")
+        desc._key_lens = (ctypes.c_int32 * B)(*[int(x) for x in key_lens])
+        desc.key_lens = ctypes.cast(desc._key_lens, ctypes.POINTER(ctypes.c_int32))
+    return desc
 
 
 def _ptr(t):
@@ -247,8 +256,8 @@ class Buffers:
     """Device buffers for one problem shape (allocated once, reused by calls)."""
 
     def __init__(self, B, H, N, d, in_dtype=torch.bfloat16, out_dtype=torch.float32,
-                 tau_mode="hist", max_iters=0, tol=0.0, force_dense=False, device="cuda"):
-        self.desc = make_desc(B, H, N, d, in_dtype, out_dtype, tau_mode, max_iters, tol, force_dense)
+                 tau_mode="hist", max_iters=0, tol=0.0, force_dense=False, device="cuda", key_lens=None):
+        self.desc = make_desc(B, H, N, d, in_dtype, out_dtype, tau_mode, max_iters, tol, force_dense, key_lens)
         n_qt, n_kt, self.bm, self.bn = entmax_attn_mask_dims(self.desc)
         dev = torch.device(device)
         self.out = torch.empty(B, H, N, d, dtype=out_dtype, device=dev)

@@ -49,6 +49,7 @@
 #include <math.h>
 #include <float.h>
 
+#include <algorithm>
 #include <climits>
 #include <mutex>
 #include <type_traits>
@@ -87,6 +88,12 @@ struct Params {
   int out_bf16;
   int pair_qt;            // row-max sweep: one workgroup per pair of causal query tiles
   int hshift;             // histogram fixed point: y in units of 2^-hshift
+  // Caller tensors: rows per head (ld >= N) and block-mask strides.  They
+  // differ from N and the mask shape only for one batch of a
+  // variable-length call, which runs as its own problem of length N inside
+  // the caller's [B, H, ld, d] tensors; workspace arrays always use N.
+  int ld, mrs;
+  long long mhs;
 };
 
 // ----------------------------------------------------------- fragments ---
@@ -674,8 +681,8 @@ __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, co
   map_tile(n_qt, P.BH, P.causal, bh, qtile);
   const int q0 = qtile * 256;
   const int wq0 = q0 + 64 * w;
-  const E* Qh = Q + (size_t)bh * N * D;
-  const E* Kh = K + (size_t)bh * N * D;
+  const E* Qh = Q + (size_t)bh * P.ld * D;
+  const E* Kh = K + (size_t)bh * P.ld * D;
 
   Frag<E> qf[2][D / 16];
   int iq[2];
@@ -803,8 +810,8 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
   // alone); otherwise one tile per workgroup, heaviest first.
   int bh, unit;
   map_tile(P.pair_qt ? (n_qt + 1) / 2 : n_qt, P.BH, P.causal && !P.pair_qt, bh, unit);
-  const __bf16* Qh = Q + (size_t)bh * N * D;
-  const __bf16* Kh = K + (size_t)bh * N * D;
+  const __bf16* Qh = Q + (size_t)bh * P.ld * D;
+  const __bf16* Kh = K + (size_t)bh * P.ld * D;
   const DT dt(Kh, N, w, lane);
   const int ktc = blk_row(P.n_kt);
 
@@ -1237,8 +1244,8 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   const bool valid = iq < N;
   const bool wave_rows = wq0 < N;
   const int r32 = qtile * kWaves + w;
-  const E* Qh = Q + (size_t)bh * N * D;
-  const E* Kh = K + (size_t)bh * N * D;
+  const E* Qh = Q + (size_t)bh * P.ld * D;
+  const E* Kh = K + (size_t)bh * P.ld * D;
   const bool dense = (P.flags & EA_FLAG_FORCE_DENSE) != 0;
 
   // histogram rows are padded by one bin so the 32 rows of a wave updating
@@ -1377,7 +1384,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   }
 
   // ---- refinement sweeps (Halley-bisection or bisection) over candidate tiles
-  uint8_t* mrow = mask_out + ((size_t)bh * P.n_q32 + (size_t)r32) * P.n_kt;
+  uint8_t* mrow = mask_out + (size_t)bh * P.mhs + (size_t)r32 * P.mrs;
   if (wave_rows) {
     for (int kt = lane; kt < P.n_kt; kt += kWave) mrow[kt] = (dense && kt < kt_end_w) ? 7 : 0;
   }
@@ -1533,8 +1540,8 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   }
 
   if (valid && h == 0) {
-    tau_out[(size_t)bh * N + iq] = tau;
-    if (iters_out) iters_out[(size_t)bh * N + iq] = (uint8_t)min(iters, 255);
+    tau_out[(size_t)bh * P.ld + iq] = tau;
+    if (iters_out) iters_out[(size_t)bh * P.ld + iq] = (uint8_t)min(iters, 255);
   }
 
   // ---- P V over the active tiles of the final mask (bf16).  Q is still in
@@ -1543,7 +1550,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   if constexpr (kFusePV) {
     __syncthreads();   // every wave's final mask bits (and the histogram is dead)
     char* vbuf = reinterpret_cast<char*>(hist);                       // 2 x [64][KS]
-    const E* Vh = V + (size_t)bh * N * D;
+    const E* Vh = V + (size_t)bh * P.ld * D;
     const float ptau = valid ? tau : INFINITY;
     f32x16 oacc[D / 32];
 #pragma unroll
@@ -1582,7 +1589,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         __syncthreads();
       }
     }
-    if (valid) store_out<D>(oacc, out, (size_t)bh * N + iq, h, P.out_bf16 != 0);
+    if (valid) store_out<D>(oacc, out, (size_t)bh * P.ld + iq, h, P.out_bf16 != 0);
   }
 }
 
@@ -1608,9 +1615,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const int wq0 = qtile * kBQW + kBQ * w;
   const int iq = wq0 + c32;
   const bool valid = iq < N;
-  const E* Qh = Q + (size_t)bh * N * D;
-  const E* Kh = K + (size_t)bh * N * D;
-  const E* Vh = kTr ? Vsrc + (size_t)bh * N * D : Vsrc + (size_t)bh * D * P.Np;
+  const E* Qh = Q + (size_t)bh * P.ld * D;
+  const E* Kh = K + (size_t)bh * P.ld * D;
+  const E* Vh = kTr ? Vsrc + (size_t)bh * P.ld * D : Vsrc + (size_t)bh * D * P.Np;
 
   char* kbuf = smem;                                 // 2 x [64][KS]
   char* vbuf = kbuf + 2 * kBK * KS;                  // 2 x V tile
@@ -1621,16 +1628,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 
   Frag<E> qf[D / 16];
   load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
-  const float tau = valid ? tau_in[(size_t)bh * N + iq] : INFINITY;
+  const float tau = valid ? tau_in[(size_t)bh * P.ld + iq] : INFINITY;
   const bool wave_has_tail = wq0 + kBQ > N;
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
 
-  const size_t mrow0 = (size_t)bh * P.n_q32 + (size_t)qtile * kWaves;
+  const uint8_t* mrow0 = mask + (size_t)bh * P.mhs + (size_t)qtile * kWaves * P.mrs;
   auto active = [&](int ww, int kt) -> bool {
-    return (qtile * kWaves + ww) < P.n_q32 && mask[(mrow0 + ww) * P.n_kt + kt] != 0;
+    return (qtile * kWaves + ww) < P.n_q32 && mrow0[(size_t)ww * P.mrs + kt] != 0;
   };
   RowTiles<E, D, kBK> sk(Kh, N, w, lane);
   RowTiles<E, D, kBK> svr(Vh, N, w, lane);   // bf16 V rows
@@ -1668,16 +1675,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       __syncthreads();
     }
   }
-  if (valid) store_out<D>(oacc, out, (size_t)bh * N + iq, h, P.out_bf16 != 0);
+  if (valid) store_out<D>(oacc, out, (size_t)bh * P.ld + iq, h, P.out_bf16 != 0);
 }
 
 // --------------------------------------------------------- transposes ---
 // [BH][N][D] -> [BH][D][Np], zero for n in [N, Np).
 template <typename E>
 __global__ __launch_bounds__(256) void k_transpose(const E* __restrict__ in, E* __restrict__ outp,
-                                                   int N, int D, int Np) {
+                                                   int N, int ld, int D, int Np) {
   __shared__ E t[64][65];
-  const E* src = in + (size_t)blockIdx.z * N * D;
+  const E* src = in + (size_t)blockIdx.z * ld * D;
   E* dst = outp + (size_t)blockIdx.z * D * Np;
   const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
@@ -1717,7 +1724,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const int wq0 = qtile * kBQW + kBQ * w;
   const int iq = wq0 + c32;
   const bool valid = iq < N;
-  const size_t hoff = (size_t)bh * N * D;
+  const size_t hoff = (size_t)bh * P.ld * D;
   const E* Kth = kTr ? nullptr : Kt + (size_t)bh * D * P.Np;
 
   // NB = 2: double-buffered tiles; NB = 1 when two copies exceed the LDS
@@ -1732,16 +1739,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   Frag<E> qf[D / 16], of[D / 16];
   load_qfrags<E, D>(qf, Q + hoff + (size_t)iq * D, valid, h);
   load_qfrags<E, D>(of, dO + hoff + (size_t)iq * D, valid, h);
-  const float tau = valid ? tau_in[(size_t)bh * N + iq] : INFINITY;
+  const float tau = valid ? tau_in[(size_t)bh * P.ld + iq] : INFINITY;
   const bool wave_has_tail = wq0 + kBQ > N;
 
   f32x16 gacc[D / 32];                               // dQ, live in the second pass only
   float num = 0.0f, den = 0.0f, dlt = 0.0f;
 
-  const size_t mrow0 = (size_t)bh * P.n_q32 + (size_t)qtile * kWaves;
+  const uint8_t* mrow0 = mask + (size_t)bh * P.mhs + (size_t)qtile * kWaves * P.mrs;
   // the wave's mask byte of tile kt (0 past the last query block)
   auto mbyte = [&](int ww, int kt) -> uint32_t {
-    return (qtile * kWaves + ww) < P.n_q32 ? (uint32_t)mask[(mrow0 + ww) * P.n_kt + kt] : 0u;
+    return (qtile * kWaves + ww) < P.n_q32 ? (uint32_t)mrow0[(size_t)ww * P.mrs + kt] : 0u;
   };
   // two bits per wave: which 32-key halves of the tile hold a probability
   auto halves = [&](int ww, int kt) -> uint32_t { return half_bits(mbyte(ww, kt)); };
@@ -1940,7 +1947,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   const int jk = kw0 + c32;
   const bool kvalid = jk < N;
   const bool wave_keys = kw0 < N;
-  const size_t hoff = (size_t)bh * N * D;
+  const size_t hoff = (size_t)bh * P.ld * D;
   const E* Qth = kTr ? nullptr : Qt + (size_t)bh * D * P.Np;
   const E* dOth = kTr ? nullptr : dOt + (size_t)bh * D * P.Np;
 
@@ -1987,7 +1994,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   // each; rows past N read as zeros and are masked by the row limits) or
   // registers of the first 32 threads
   __amdgpu_buffer_rsrc_t rs_td = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(w == 0 ? tau_in + (size_t)bh * N : delta_in + (size_t)bh * N), (short)0, N * 4,
+      const_cast<float*>(w == 0 ? tau_in + (size_t)bh * P.ld : delta_in + (size_t)bh * N), (short)0, N * 4,
       0x00020000);
   float sta = 0.0f, sde = 0.0f;
   auto load = [&](int r, int b) {
@@ -2010,7 +2017,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       }
       if (threadIdx.x < kBQ) {
         const int qi = qb0 + threadIdx.x;
-        sta = qi < N ? tau_in[(size_t)bh * N + qi] : INFINITY;
+        sta = qi < N ? tau_in[(size_t)bh * P.ld + qi] : INFINITY;
         sde = qi < N ? delta_in[(size_t)bh * N + qi] : 0.0f;
       }
     }
@@ -2369,6 +2376,50 @@ __global__ __launch_bounds__(kThreads) void k_entmax_rows(const EI* __restrict__
   }
 }
 
+// ------------------------------------------------------------ padding ---
+// Variable-length calls: each batch b sees only its first L keys and query
+// rows.  A query row past L sees no key at all: its output row is 0, tau is
+// +inf (so every p = [x - tau]_+^beta is 0) and its sweep count 0; keys past L
+// get zero dK and dV, rows past L zero dQ, and every block-mask entry outside
+// the batch's [ceil(L/32)] x [ceil(L/64)] tiles is 0.  These kernels write
+// exactly those entries of one batch (all H heads) with plain stores.
+template <typename EO>
+__global__ __launch_bounds__(256) void k_pad_fwd(EO* __restrict__ out, float* __restrict__ tau,
+                                                 uint8_t* __restrict__ iters, uint8_t* __restrict__ mask,
+                                                 int H, int N, int L, int D, int n_q32, int n_kt, int n_q32L,
+                                                 int n_ktL) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long t0 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long rows = (long long)H * (N - L);
+  for (long long e = t0; e < rows * D; e += stride) {
+    const long long r = e / D, h = r / (N - L), i = L + r % (N - L);
+    out[((size_t)h * N + i) * D + e % D] = (EO)0.0f;
+  }
+  for (long long r = t0; r < rows; r += stride) {
+    const long long h = r / (N - L), i = L + r % (N - L);
+    tau[(size_t)h * N + i] = INFINITY;
+    if (iters) iters[(size_t)h * N + i] = 0;
+  }
+  const long long me = (long long)H * n_q32 * n_kt;
+  for (long long e = t0; e < me; e += stride) {
+    const long long kt = e % n_kt, r = (e / n_kt) % n_q32;
+    if (r >= n_q32L || kt >= n_ktL) mask[e] = 0;
+  }
+}
+template <typename EO>
+__global__ __launch_bounds__(256) void k_pad_bwd(EO* __restrict__ dq, EO* __restrict__ dk, EO* __restrict__ dv,
+                                                 int H, int N, int L, int D) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  const long long n = (long long)H * (N - L) * D;
+  for (long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+    const long long r = e / D, h = r / (N - L), i = L + r % (N - L);
+    const size_t off = ((size_t)h * N + i) * D + e % D;
+    dq[off] = (EO)0.0f;
+    dk[off] = (EO)0.0f;
+    dv[off] = (EO)0.0f;
+  }
+}
+
 // =============================================================== host ===
 
 struct Shape {
@@ -2379,6 +2430,23 @@ struct Shape {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kMaxN = 1 << 20;
+
+Shape shape_of(int B, int H, int N, int d, int esz) {
+  Shape s;
+  s.B = B;
+  s.H = H;
+  s.N = N;
+  s.d = d;
+  s.esz = esz;
+  s.n_kt = (N + kBK - 1) / kBK;
+  s.n_q32 = (N + kBQ - 1) / kBQ;
+  s.n_qt128 = (N + kBQW - 1) / kBQW;
+  s.n_qt256 = (N + 255) / 256;
+  s.n_kt128 = (N + 127) / 128;
+  s.Np = s.n_kt * kBK;
+  s.BH = B * H;
+  return s;
+}
 
 int check_desc(const ea_desc* desc, Shape* s) {
   if (!desc) return EA_ERR_NULL;
@@ -2392,20 +2460,11 @@ int check_desc(const ea_desc* desc, Shape* s) {
   if (desc->max_iters < 0 || desc->max_iters > 250) return EA_ERR_UNSUPPORTED;
   if (!(desc->tol >= 0.0f) || !(desc->tol < 1.0f)) return EA_ERR_UNSUPPORTED;
   if (desc->flags & ~EA_FLAG_FORCE_DENSE) return EA_ERR_UNSUPPORTED;
-  if (s) {
-    s->B = desc->B;
-    s->H = desc->H;
-    s->N = desc->N;
-    s->d = desc->d;
-    s->esz = desc->in_dtype == EA_BF16 ? 2 : 4;
-    s->n_kt = (desc->N + kBK - 1) / kBK;
-    s->n_q32 = (desc->N + kBQ - 1) / kBQ;
-    s->n_qt128 = (desc->N + kBQW - 1) / kBQW;
-    s->n_qt256 = (desc->N + 255) / 256;
-    s->n_kt128 = (desc->N + 127) / 128;
-    s->Np = s->n_kt * kBK;
-    s->BH = desc->B * desc->H;
+  if (desc->key_lens) {
+    for (int b = 0; b < desc->B; ++b)
+      if (desc->key_lens[b] < 0 || desc->key_lens[b] > desc->N) return EA_ERR_SHAPE;
   }
+  if (s) *s = shape_of(desc->B, desc->H, desc->N, desc->d, desc->in_dtype == EA_BF16 ? 2 : 4);
   return EA_OK;
 }
 
@@ -2476,6 +2535,9 @@ Params make_params(const ea_desc* desc, const Shape& s, float alpha, int causal)
   P.out_bf16 = desc->out_dtype == EA_BF16 ? 1 : 0;
   P.pair_qt = 0;
   P.hshift = hist_shift(s.N);
+  P.ld = s.N;
+  P.mrs = s.n_kt;
+  P.mhs = (long long)s.n_q32 * s.n_kt;
   return P;
 }
 
@@ -2565,7 +2627,7 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
 
   tm.begin(EA_STAGE_FWD_PREP);
   if constexpr (!kTr) {
-    if ((rc = launch(k_transpose<E>, dim3(s.Np / 64, D / 64, s.BH), dim3(256), 0, st, V, Vt, s.N, D, s.Np)) != EA_OK)
+    if ((rc = launch(k_transpose<E>, dim3(s.Np / 64, D / 64, s.BH), dim3(256), 0, st, V, Vt, s.N, P.ld, D, s.Np)) != EA_OK)
       return rc;
   }
   tm.end(EA_STAGE_FWD_PREP);
@@ -2631,9 +2693,9 @@ int launch_bwd(const Shape& s, Params P, const void* q, const void* k, const voi
   tm.begin(EA_STAGE_BWD_PREP);
   if constexpr (!kTr) {
     const dim3 tg(s.Np / 64, D / 64, s.BH);
-    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, K, Kt, s.N, D, s.Np)) != EA_OK) return rc;
-    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, Q, Qt, s.N, D, s.Np)) != EA_OK) return rc;
-    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, dO, dOt, s.N, D, s.Np)) != EA_OK) return rc;
+    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, K, Kt, s.N, P.ld, D, s.Np)) != EA_OK) return rc;
+    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, Q, Qt, s.N, P.ld, D, s.Np)) != EA_OK) return rc;
+    if ((rc = launch(k_transpose<E>, tg, dim3(256), 0, st, dO, dOt, s.N, P.ld, D, s.Np)) != EA_OK) return rc;
   }
   tm.end(EA_STAGE_BWD_PREP);
 
@@ -2756,6 +2818,99 @@ size_t fwd_workspace_bytes(const Shape& s) { return transposed_bytes(s) + row_by
     }                                                                                 \
   } while (0)
 
+int run_fwd(const Shape& s, const Params& P, const ea_desc* desc, float alpha, const void* q, const void* k,
+            const void* v, void* out, float* tau, uint8_t* block_mask, uint8_t* tau_iters, void* ws,
+            hipStream_t hs, StageTimer tm) {
+  EA_DISPATCH(launch_fwd, s, P, q, k, v, out, tau, block_mask, tau_iters, ws, hs, tm);
+}
+int run_bwd(const Shape& s, const Params& P, const ea_desc* desc, float alpha, const void* q, const void* k,
+            const void* v, const void* dout, const float* tau, const uint8_t* block_mask, void* dq, void* dk,
+            void* dv, void* ws, hipStream_t hs, StageTimer tm) {
+  EA_DISPATCH(launch_bwd, s, P, q, k, v, dout, tau, block_mask, dq, dk, dv, ws, hs, tm);
+}
+
+unsigned pad_grid(long long n) { return (unsigned)std::min<long long>(std::max<long long>((n + 255) / 256, 1), 4096); }
+
+// The whole forward: one problem, or with key_lens one problem per batch on
+// the same tensors (row stride N, mask strides of the full shape) followed by
+// the padding of that batch.  Stage events are recorded for one problem only.
+int forward_all(const Shape& s, const ea_desc* desc, float alpha, int causal, const void* q, const void* k,
+                const void* v, void* out, float* tau, uint8_t* block_mask, uint8_t* tau_iters, void* ws,
+                hipStream_t hs) {
+  if (!desc->key_lens) {
+    return run_fwd(s, make_params(desc, s, alpha, causal), desc, alpha, q, k, v, out, tau, block_mask, tau_iters,
+                   ws, hs, StageTimer{desc->events, hs});
+  }
+  const size_t hrow = (size_t)s.H * s.N;                   // rows per batch
+  const size_t ie = s.esz, oe = desc->out_dtype == EA_BF16 ? 2 : 4;
+  const size_t mb = (size_t)s.H * s.n_q32 * s.n_kt;          // mask bytes per batch
+  for (int b = 0; b < s.B; ++b) {
+    const int L = desc->key_lens[b];
+    const Shape sb = shape_of(1, s.H, L, s.d, s.esz);
+    Params P = make_params(desc, sb, alpha, causal);
+    P.ld = s.N;
+    P.mrs = s.n_kt;
+    P.mhs = (long long)s.n_q32 * s.n_kt;
+    const size_t off = (size_t)b * hrow * s.d;
+    char* ob = static_cast<char*>(out) + off * oe;
+    uint8_t* mkb = block_mask + b * mb;
+    float* tb = tau + b * hrow;
+    uint8_t* ib = tau_iters ? tau_iters + b * hrow : nullptr;
+    int rc = run_fwd(sb, P, desc, alpha, static_cast<const char*>(q) + off * ie, static_cast<const char*>(k) + off * ie,
+                     static_cast<const char*>(v) + off * ie, ob, tb, mkb, ib, ws, hs, StageTimer{nullptr, hs});
+    if (rc != EA_OK) return rc;
+    const dim3 g(pad_grid((long long)s.H * std::max(s.N - L, 1) * s.d + (long long)mb));
+    const int nq = (L + kBQ - 1) / kBQ, nk = (L + kBK - 1) / kBK;
+    if (oe == 2)
+      rc = launch(k_pad_fwd<__bf16>, g, dim3(256), 0, hs, reinterpret_cast<__bf16*>(ob), tb, ib, mkb, s.H, s.N, L,
+                  s.d, s.n_q32, s.n_kt, nq, nk);
+    else
+      rc = launch(k_pad_fwd<float>, g, dim3(256), 0, hs, reinterpret_cast<float*>(ob), tb, ib, mkb, s.H, s.N, L,
+                  s.d, s.n_q32, s.n_kt, nq, nk);
+    if (rc != EA_OK) return rc;
+  }
+  return EA_OK;
+}
+
+int backward_all(const Shape& s, const ea_desc* desc, float alpha, int causal, const void* q, const void* k,
+                 const void* v, const void* dout, const float* tau, const uint8_t* block_mask, void* dq, void* dk,
+                 void* dv, void* ws, hipStream_t hs) {
+  if (!desc->key_lens) {
+    return run_bwd(s, make_params(desc, s, alpha, causal), desc, alpha, q, k, v, dout, tau, block_mask, dq, dk, dv,
+                   ws, hs, StageTimer{desc->events, hs});
+  }
+  const size_t hrow = (size_t)s.H * s.N;
+  const size_t ie = s.esz, oe = desc->out_dtype == EA_BF16 ? 2 : 4;
+  const size_t mb = (size_t)s.H * s.n_q32 * s.n_kt;
+  for (int b = 0; b < s.B; ++b) {
+    const int L = desc->key_lens[b];
+    const Shape sb = shape_of(1, s.H, L, s.d, s.esz);
+    Params P = make_params(desc, sb, alpha, causal);
+    P.ld = s.N;
+    P.mrs = s.n_kt;
+    P.mhs = (long long)s.n_q32 * s.n_kt;
+    const size_t off = (size_t)b * hrow * s.d;
+    char* qb = static_cast<char*>(dq) + off * oe;
+    char* kb = static_cast<char*>(dk) + off * oe;
+    char* vb = static_cast<char*>(dv) + off * oe;
+    int rc = run_bwd(sb, P, desc, alpha, static_cast<const char*>(q) + off * ie, static_cast<const char*>(k) + off * ie,
+                     static_cast<const char*>(v) + off * ie, static_cast<const char*>(dout) + off * ie,
+                     tau + b * hrow, block_mask + b * mb, qb, kb, vb, ws, hs, StageTimer{nullptr, hs});
+    if (rc != EA_OK) return rc;
+    if (L < s.N) {
+      const dim3 g(pad_grid((long long)s.H * (s.N - L) * s.d));
+      if (oe == 2)
+        rc = launch(k_pad_bwd<__bf16>, g, dim3(256), 0, hs, reinterpret_cast<__bf16*>(qb), reinterpret_cast<__bf16*>(kb),
+                    reinterpret_cast<__bf16*>(vb), s.H, s.N, L, s.d);
+      else
+        rc = launch(k_pad_bwd<float>, g, dim3(256), 0, hs, reinterpret_cast<float*>(qb), reinterpret_cast<float*>(kb),
+                    reinterpret_cast<float*>(vb), s.H, s.N, L, s.d);
+      if (rc != EA_OK) return rc;
+    }
+  }
+  return EA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -2792,10 +2947,8 @@ int entmax_attn_fwd(const void* q, const void* k, const void* v, float alpha, in
       return EA_ERR_ALIGN;
     if (ws_bytes < workspace_bytes(s)) return EA_ERR_WORKSPACE;
   }
-  Params P = make_params(desc, s, alpha, causal);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  EA_DISPATCH(launch_fwd, s, P, q, k, v, out, tau, block_mask, tau_iters, ws, hs,
-              StageTimer{desc->events, hs});
+  return forward_all(s, desc, alpha, causal, q, k, v, out, tau, block_mask, tau_iters, ws,
+                     static_cast<hipStream_t>(stream));
 }
 
 int entmax_attn_fwd_static(const void* q, const void* k, const void* v, float alpha, int causal, void* out,
@@ -2814,10 +2967,8 @@ int entmax_attn_fwd_static(const void* q, const void* k, const void* v, float al
     if (fwd_workspace_bytes(s) > kStaticScratchBytes) return EA_ERR_WORKSPACE;
     if ((st = static_scratch(&ws)) != EA_OK) return st;
   }
-  Params P = make_params(desc, s, alpha, causal);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  EA_DISPATCH(launch_fwd, s, P, q, k, v, out, tau, block_mask, tau_iters, ws, hs,
-              StageTimer{desc->events, hs});
+  return forward_all(s, desc, alpha, causal, q, k, v, out, tau, block_mask, tau_iters, ws,
+                     static_cast<hipStream_t>(stream));
 }
 
 int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, int causal,
@@ -2835,10 +2986,8 @@ int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, in
       return EA_ERR_ALIGN;
     if (ws_bytes < workspace_bytes(s)) return EA_ERR_WORKSPACE;
   }
-  Params P = make_params(desc, s, alpha, causal);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  EA_DISPATCH(launch_bwd, s, P, q, k, v, dout, tau, block_mask, dq, dk, dv, ws, hs,
-              StageTimer{desc->events, hs});
+  return backward_all(s, desc, alpha, causal, q, k, v, dout, tau, block_mask, dq, dk, dv, ws,
+                      static_cast<hipStream_t>(stream));
 }
 
 int entmax_rows(const void* s, float alpha, void* p, float* tau, uint8_t* tau_iters, const ea_rows_desc* desc,

@@ -50,7 +50,7 @@ extern "C" {
 /* Status codes (0 = success). */
 #define EA_OK               0
 #define EA_ERR_NULL        -1   /* a required pointer is NULL */
-#define EA_ERR_SHAPE       -2   /* B, H < 1, N < 0, or d not in {64, 128} */
+#define EA_ERR_SHAPE       -2   /* B, H < 1, N < 0, d not in {64, 128}, or a key length outside [0, N] */
 #define EA_ERR_DTYPE       -3   /* unknown in_dtype / out_dtype */
 #define EA_ERR_ALPHA       -4   /* alpha outside (1, 2] or not finite */
 #define EA_ERR_ALIGN       -5   /* a tensor pointer is not 16-byte aligned */
@@ -87,6 +87,15 @@ typedef struct {
    * events[2s+1], recorded on `stream`; stages a call does not run are not
    * recorded.  The library never creates or destroys events. */
   void* const* events;
+  /* Variable-length batches (key padding), "AdaSplash: Adaptive Sparse Flash
+   * Attention", "Downstream Task Performance" (encoder models): NULL, or a
+   * host array of B lengths 0 <= L_b <= N, read during the call.  Batch b
+   * then attends over its first L_b keys only, and its query rows past L_b
+   * see no key: their output rows are 0, tau = +inf (every p is 0), their
+   * sweep count 0; dQ rows and dK / dV rows past L_b are 0, and block-mask
+   * entries outside the batch's first ceil(L_b/32) x ceil(L_b/64) tiles are 0.
+   * The stage events are not recorded for such calls. */
+  const int32_t* key_lens;
 } ea_desc;
 
 /* Stages, for the timing hook. */

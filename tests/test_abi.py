@@ -38,8 +38,8 @@ def test_header_constants_match_binding():
 
 
 def test_desc_struct_layout():
-    # int32 x 9 + float + pointer, natural alignment
-    assert ctypes.sizeof(Bd.EaDesc) == 48
+    # int32 x 9 + float + two pointers, natural alignment
+    assert ctypes.sizeof(Bd.EaDesc) == 56
     # int64 + int32 x 5 + float
     assert ctypes.sizeof(Bd.EaRowsDesc) == 32
 
@@ -213,3 +213,18 @@ def test_binding_rejects_mismatched_tensors():
         fwd()
     with pytest.raises(ValueError, match="dtype"):
         Bd.entmax_attn_bwd(q, q, q, 1.5, 1, q, tau, mask, out, out, out.to(torch.bfloat16), d, None)
+
+
+def test_key_lens_checked_before_launch():
+    """A key length outside [0, N] is refused with EA_ERR_SHAPE before any
+    GPU work; valid lengths pass the descriptor checks."""
+    lib = A.load_library()
+    ok = A.make_desc(3, 2, 100, 64, key_lens=[100, 7, 0])
+    assert A.entmax_attn_workspace_bytes(ok) > 0
+    for bad in ([101, 5, 5], [5, -1, 5]):
+        d = A.make_desc(3, 2, 100, 64, key_lens=bad)
+        assert A.entmax_attn_workspace_bytes(d) == 0
+        p = ctypes.c_void_p(256)
+        assert lib.entmax_attn_fwd(p, p, p, 1.5, 1, p, p, p, None, ctypes.byref(d), p, 1 << 20, None) == -2
+    with pytest.raises(ValueError):
+        A.make_desc(3, 2, 100, 64, key_lens=[1, 2])

@@ -255,3 +255,42 @@ def test_tied_keys_beyond_65536():
             PT.check_close("dk[last 512]", res["dk"][0, 0, i0:], gk[i0:], tol)
             PT.check_close("dv[last 512]", res["dv"][0, 0, i0:], gv[i0:], tol)
     assert np.all(res["iters"] >= 1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("name,d", [("encoder_8k", 64), ("planted_16k", 128)])
+def test_variable_length_batches(name, d, causal):
+    """Key padding: batch b attends over its first L_b keys only.  Rows below
+    L_b match the oracle on the truncated sequence (forward and backward);
+    rows past L_b give out = 0, tau = +inf, zero gradients and zero mask
+    entries; L = 0 and L = N are included."""
+    lens = [700, 333, 0, 65]
+    w = G.workload(name, B=4, H=2, N=700, d=d, causal=causal)
+    x = G.make_inputs(w)
+    print(f"\n[varlen] {name} d={d} causal={causal} lens={lens}", flush=True)
+    bufs = A.Buffers(w.B, w.H, w.N, w.d, torch.bfloat16, torch.float32, "hist", key_lens=lens)
+    dev = [PT.to_device(x[n], "bf16") for n in ("q", "k", "v", "dout")]
+    bufs.forward(dev[0], dev[1], dev[2], w.alpha, w.causal)
+    bufs.backward(dev[0], dev[1], dev[2], dev[3], w.alpha, w.causal)
+    torch.cuda.synchronize()
+    got = {n: getattr(bufs, n).float().cpu().numpy() for n in ("out", "tau", "mask", "dq", "dk", "dv", "iters")}
+    for b, L in enumerate(lens):
+        if L > 0:
+            q, k, v, do = (x[n][b:b + 1, :, :L] for n in ("q", "k", "v", "dout"))
+            out_ref, tau_ref = O.attention_forward(q, k, v, w.alpha, w.causal)
+            PT.check_tau(got["tau"][b:b + 1, :, :L], tau_ref)
+            PT.check_close(f"out[b{b}]", got["out"][b:b + 1, :, :L], out_ref, 1e-2)
+            PT.check_support(q, k, w.alpha, w.causal, got["tau"][b:b + 1, :, :L], tau_ref)
+            margins = O.tile_margins(q, k, w.alpha, w.causal, tau_ref, MASK_BM, MASK_BN)
+            nq, nk = margins.shape[-2:]
+            PT.check_mask(got["mask"][b:b + 1, :, :nq, :nk], margins)
+            dq, dk, dv = O.attention_backward(q, k, v, do, w.alpha, w.causal, tau=tau_ref)
+            for nm, ref in (("dq", dq), ("dk", dk), ("dv", dv)):
+                PT.check_close(f"{nm}[b{b}]", got[nm][b:b + 1, :, :L], ref, 1e-2)
+        assert np.all(got["out"][b, :, L:] == 0.0) and np.all(np.isposinf(got["tau"][b, :, L:]))
+        assert np.all(got["iters"][b, :, L:] == 0)
+        for nm in ("dq", "dk", "dv"):
+            assert np.all(got[nm][b, :, L:] == 0.0), nm
+        nq, nk = -(-L // 32), -(-L // 64)
+        m = got["mask"][b]
+        assert np.all(m[:, nq:, :] == 0) and np.all(m[:, :, nk:] == 0)
