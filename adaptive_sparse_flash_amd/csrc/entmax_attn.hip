@@ -2370,7 +2370,7 @@ __global__ __launch_bounds__(kThreads) void k_entmax_rows(const EI* __restrict__
       store4(prow, e, n, vec, o);
     });
     if (lane == 0) {
-      tau_out[r] = empty ? NAN : tau;
+      tau_out[r] = empty ? INFINITY : tau;
       if (iters_out) iters_out[r] = (uint8_t)min(iters, 255);
     }
   }

@@ -194,7 +194,7 @@ int entmax_attn_bwd(const void* q, const void* k, const void* v, float alpha, in
  *   x_j = (alpha - 1) s_rj,  tau_r: sum_j [x_j - tau_r]_+^(1/(alpha-1)) = 1,
  *   p_rj = [x_j - tau_r]_+^(1/(alpha-1)).
  * -inf scores are masked entries (p = 0, not counted); a row with no finite
- * score gets tau = NaN and p = 0.  tau_mode selects the start and the steps
+ * score gets tau = +inf and p = 0.  tau_mode selects the start and the steps
  * exactly as for the attention forward; tau_iters counts the sweeps that
  * evaluated f (the row-max and histogram passes are not counted).
  *  s          [rows, n] in_dtype, dense row-major        (read)

@@ -67,14 +67,14 @@ def test_rows_bf16_in_and_out():
 def test_rows_masked_tied_onehot():
     n = 1500
     s = G.make_score_rows(8, n, scale=2.0, seed=11, masked=0.3)
-    s[1, :] = -np.inf                     # nothing visible: tau NaN, p = 0
+    s[1, :] = -np.inf                     # nothing visible: tau = +inf, p = 0
     s[2, :] = 0.25                        # all tied: p = 1/n
     s[3, :] = -np.inf
     s[3, 17] = 1.0                        # one visible entry: p = 1
     s[4, :] = -3.0
     s[4, 5] = 3.0                         # one-hot: the top leads by more than 1/(alpha-1)
     p, tau, it = run_rows(s, 1.5, "hist")
-    assert np.isnan(tau[1]) and np.all(p[1] == 0.0)
+    assert np.isposinf(tau[1]) and np.all(p[1] == 0.0)
     np.testing.assert_allclose(p[2], 1.0 / n, rtol=1e-4)
     assert p[3, 17] == pytest.approx(1.0, abs=1e-6) and p[3].sum() == pytest.approx(1.0, abs=1e-6)
     assert p[4, 5] == pytest.approx(1.0, abs=1e-6)
