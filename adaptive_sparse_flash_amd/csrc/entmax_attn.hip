@@ -1210,7 +1210,8 @@ __device__ __forceinline__ void hist_start(const unsigned long long* hr, float w
 // mask.  Dynamic LDS: K double buffer | histogram [128][BINS*2+2] u64 |
 // list i16[kChunk] | wave bits u8[kChunk] | flags u8[kChunk] |
 // candidate bits u32[4][n_words] | counter | final mask bits u32[4][n_words] |
-// bits of tiles above the lower bracket end u32[4][n_words].
+// bits of tiles above the lower bracket end u32[4][n_words] | bits of the two
+// 32-key halves of active tiles u32[2][4][n_words].
 constexpr int kChunk = 512;    // key tiles listed at once
 
 template <typename E, int D>
@@ -1261,6 +1262,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   int* counter = reinterpret_cast<int*>(cbits + kWaves * n_words);
   uint32_t* mbits = reinterpret_cast<uint32_t*>(counter + 16);        // [4][n_words] final mask
   uint32_t* lbits = mbits + kWaves * n_words;                         // [4][n_words] tiles above lo
+  uint32_t* hbits = lbits + kWaves * n_words;                         // [2][4][n_words] live halves
 
   const int wq_last = min(N - 1, wq0 + kBQ - 1);
   const int kt_end_w = !wave_rows ? 0 : (P.causal ? wq_last / kBK + 1 : P.n_kt);
@@ -1384,16 +1386,15 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   }
 
   // ---- refinement sweeps (Halley-bisection or bisection) over candidate tiles
+  // The final mask is kept as bits in LDS (the tile, and each 32-key half)
+  // and written to block_mask after the sweeps; the P V epilogue reads it too.
   uint8_t* mrow = mask_out + (size_t)bh * P.mhs + (size_t)r32 * P.mrs;
-  if (wave_rows) {
-    for (int kt = lane; kt < P.n_kt; kt += kWave) mrow[kt] = (dense && kt < kt_end_w) ? 7 : 0;
-  }
-  if constexpr (kFusePV) {
-    // the same mask as bits in LDS for the P V epilogue
-    for (int e = lane; e < n_words; e += kWave) {
-      const int nv = min(max(kt_end_w - 32 * e, 0), 32);
-      mbits[w * n_words + e] = dense ? (nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u)) : 0u;
-    }
+  for (int e = lane; e < n_words; e += kWave) {
+    const int nv = min(max(kt_end_w - 32 * e, 0), 32);
+    const uint32_t vis = dense ? (nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u)) : 0u;
+    mbits[w * n_words + e] = vis;
+    hbits[w * n_words + e] = vis;
+    hbits[(kWaves + w) * n_words + e] = vis;
   }
   const int max_iters = P.max_iters;
   // The candidate tiles only shrink between refinement sweeps.  When the
@@ -1401,6 +1402,11 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   // from here), they are copied once and every sweep reads them in place: no
   // list rebuild, copy or barrier per tile.
   constexpr int kResident = 2 + tau_region_bytes<E, D>(BINS) / (kBK * KS);
+  // streaming sweeps: a ring over the same slots where tiles arrive by the
+  // LDS copy engine (bf16, d = 128); register-staged tiles keep two buffers
+  constexpr bool kDMA = sizeof(E) == 2 && D == 128;
+  constexpr int kRing = kDMA ? (kResident < 4 ? kResident : 4) : 2;
+  constexpr int kTileRowsPerWave = kBK / kWaves;   // copy instructions per wave and tile
   auto slot = [&](int i) -> char* {
     return i < 2 ? kbuf + i * kBK * KS : reinterpret_cast<char*>(hist) + (i - 2) * kBK * KS;
   };
@@ -1423,11 +1429,32 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     if (wave_busy && !dense) {
       // this sweep rewrites the wave's mask and its tiles above lo
       for (int e = lane; e < n_words; e += kWave) {
-        if (kFusePV) mbits[w * n_words + e] = 0u;
+        mbits[w * n_words + e] = 0u;
+        hbits[w * n_words + e] = 0u;
+        hbits[(kWaves + w) * n_words + e] = 0u;
         lbits[w * n_words + e] = 0u;
       }
     }
     float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
+    // This wave's bits of the 32-tile word it is walking (final mask and tiles
+    // above lo), kept in wave-uniform registers and written to LDS when the
+    // walk leaves the word: an LDS write inside the tile loop would make the
+    // wave wait for the next tile's copy in flight (the compiler cannot tell
+    // the two LDS destinations apart), which would expose the copy's latency.
+    // Tiles are listed in increasing order and a word never spans two list
+    // chunks, so every word is written at most once per sweep.
+    int bit_wd = -1;
+    uint32_t m_word = 0u, l_word = 0u, h0_word = 0u, h1_word = 0u;
+    auto flush_bits = [&]() {
+      if (bit_wd >= 0 && lane == 0) {
+        mbits[w * n_words + bit_wd] = m_word;
+        hbits[w * n_words + bit_wd] = h0_word;
+        hbits[(kWaves + w) * n_words + bit_wd] = h1_word;
+        lbits[w * n_words + bit_wd] = l_word;
+      }
+      bit_wd = -1;
+      m_word = l_word = h0_word = h1_word = 0u;
+    };
     // f, f', f'' terms of key tile kt (staged at kl) and its mask bits
     auto sweep_tile = [&](int kt, const char* kl) {
       auto body = [&](auto masked) {
@@ -1448,16 +1475,21 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
           const bool any0 = __ballot(cnt_at[1] > cnt_at[0]) != 0ull;
           const bool any1 = __ballot(cnt_at[2] > cnt_at[1]) != 0ull;
           const bool any = any0 || any1;
-          if (lane == (kt & (kWave - 1)))   // same lane as the zero fill
-            mrow[kt] = any ? (uint8_t)(1u | (any0 ? 2u : 0u) | (any1 ? 4u : 0u)) : 0;
-          if (kFusePV && any && lane == 0) atomicOr(&mbits[w * n_words + (kt >> 5)], 1u << (kt & 31));
           // does the tile hold a score above some row's lower bracket end?
           float mx = fmax_nan(acc[0][0], acc[1][0]);
 #pragma unroll
           for (int j = 1; j < 16; ++j) mx = fmax_nan(mx, fmax_nan(acc[0][j], acc[1][j]));
           // (the ballot runs on every lane: it must see every row)
           const bool above = __ballot(fmaf(mx, P.scale, -lo) > 0.0f) != 0ull;
-          if (above && lane == 0) atomicOr(&lbits[w * n_words + (kt >> 5)], 1u << (kt & 31));
+          const int wd = __builtin_amdgcn_readfirstlane(kt >> 5);
+          if (wd != bit_wd) {
+            flush_bits();
+            bit_wd = wd;
+          }
+          if (any) m_word |= 1u << (kt & 31);
+          if (any0) h0_word |= 1u << (kt & 31);
+          if (any1) h1_word |= 1u << (kt & 31);
+          if (above) l_word |= 1u << (kt & 31);
         }
       };
       if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
@@ -1468,21 +1500,45 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     if (n_res >= 0) {
       for (int i = 0; i < n_res; ++i)
         if (wave_busy && cand(w, list[i])) sweep_tile(list[i], slot(i));
+      flush_bits();
     } else {
       for (int base = 0; base < kt_end; base += kChunk) {
         const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
         RowTiles<E, D, kBK> st(Kh, N, w, lane);
-        if (n > 0) {
-          st.fetch(kbuf, (base + list[0]) * kBK);
-          st.commit(kbuf);
-        }
-        __syncthreads();
-        for (int i = 0; i < n; ++i) {
-          if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
-          if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(base + list[i], kbuf + (i & 1) * kBK * KS);
-          if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
+        if constexpr (kRing > 2) {
+          // Copy ring of kRing tile slots (the histogram's space holds two of
+          // them): tile i sits in slot i % kRing and up to kRing - 1 copies are
+          // in flight, so a copy has several tiles' work to land.  Nothing else
+          // touches vector memory in this loop, so the wave's outstanding
+          // copies are counted exactly.
+#pragma unroll
+          for (int j = 0; j < kRing - 1; ++j)
+            if (j < n) st.fetch(slot(j), (base + list[j]) * kBK);
+          for (int i = 0; i < n; ++i) {
+            // tile i has landed once at most the copies of tiles i+1 .. are in flight
+            const int ahead = min(kRing - 2, n - 1 - i);
+            if (ahead >= 2) wait_vmcnt<2 * kTileRowsPerWave>();
+            else if (ahead == 1) wait_vmcnt<kTileRowsPerWave>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();   // every wave's part of tile i; slot of tile i-1 free
+            if (i + kRing - 1 < n) st.fetch(slot((i + kRing - 1) % kRing), (base + list[i + kRing - 1]) * kBK);
+            if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(base + list[i], slot(i % kRing));
+          }
           __syncthreads();
+        } else {
+          if (n > 0) {
+            st.fetch(kbuf, (base + list[0]) * kBK);
+            st.commit(kbuf);
+          }
+          __syncthreads();
+          for (int i = 0; i < n; ++i) {
+            if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
+            if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(base + list[i], kbuf + (i & 1) * kBK * KS);
+            if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
+            __syncthreads();
+          }
         }
+        flush_bits();
       }
     }
     F0 += __shfl_xor(F0, 32);
@@ -1539,6 +1595,17 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     }
   }
 
+  // block_mask row of this wave from the final bits (every tile, so no zero fill)
+  if (wave_rows) {
+    for (int kt = lane; kt < P.n_kt; kt += kWave) {
+      const uint32_t b = 1u << (kt & 31), e = (uint32_t)(kt >> 5);
+      const bool m = mbits[w * n_words + e] & b;
+      const uint32_t v = m ? (1u | ((hbits[w * n_words + e] & b) ? 2u : 0u) |
+                              ((hbits[(kWaves + w) * n_words + e] & b) ? 4u : 0u))
+                           : 0u;
+      mrow[kt] = (uint8_t)v;
+    }
+  }
   if (valid && h == 0) {
     tau_out[(size_t)bh * P.ld + iq] = tau;
     if (iters_out) iters_out[(size_t)bh * P.ld + iq] = (uint8_t)min(iters, 255);
@@ -2611,7 +2678,7 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   // every LDS size is checked and allowed before anything is enqueued
   const size_t rm_lds = kTr ? (size_t)2 * kRowmaxTPS * DirectTile<D>::BYTES : (size_t)2 * kBK * KS;
   const size_t tau_lds = (size_t)2 * kBK * KS + (size_t)tau_region_bytes<E, D>(BINS) + 4 * kChunk +
-                         (size_t)3 * kWaves * ((s.n_kt + 31) / 32) * 4 + 64;
+                         (size_t)5 * kWaves * ((s.n_kt + 31) / 32) * 4 + 64;
   constexpr int VT = D * (kBK * (int)sizeof(E) + 16);
   const size_t pv_lds = (size_t)2 * kBK * KS + (size_t)2 * VT + 4 * kChunk + 16;
   auto ktau = k_tau<E, D, AK, BINS>;
