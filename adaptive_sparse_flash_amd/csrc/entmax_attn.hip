@@ -87,7 +87,7 @@ struct Params {
   float tol;
   int out_bf16;
   int pair_qt;            // row-max sweep: one workgroup per pair of causal query tiles
-  int hshift;             // histogram fixed point: y in units of 2^-hshift
+  int hshift;             // histogram fixed point: Y = floor(y (2^hshift - 1))
   // Caller tensors: rows per head (ld >= N) and block-mask strides.  They
   // differ from N and the mask shape only for one batch of a
   // variable-length call, which runs as its own problem of length N inside
@@ -118,11 +118,6 @@ __device__ __forceinline__ void ld8(Frag<float>& f, const float* p) {
   f.b = *reinterpret_cast<const f32x4*>(p + 4);
 }
 // two runs of 4 consecutive elements (transposed tiles, permuted key order)
-__device__ __forceinline__ void ld4x2(Frag<__bf16>& f, const __bf16* p0, const __bf16* p1) {
-  bf16x4 a = *reinterpret_cast<const bf16x4*>(p0);
-  bf16x4 b = *reinterpret_cast<const bf16x4*>(p1);
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 __device__ __forceinline__ void ld4x2(Frag<float>& f, const float* p0, const float* p1) {
   f.a = *reinterpret_cast<const f32x4*>(p0);
   f.b = *reinterpret_cast<const f32x4*>(p1);
@@ -135,23 +130,74 @@ __device__ __forceinline__ void ld4x2(Frag<float>& f, const float* p0, const flo
 template <typename E, int D>
 constexpr int row_stride() { return D * (int)sizeof(E) + (sizeof(E) == 2 ? 48 : 16); }
 
-// Operand fragment whose 8 contraction elements run down one column of a
+// Operand fragments whose 8 contraction elements run down one column of a
 // row-major bf16 LDS tile: rows r0 + {0,1,2,3} and r0 + 8 + {0,1,2,3} (the
-// permuted key order of the score accumulators), column col0 + (lane & 31).
-// ds_read_b64_tr_b16 gives lane i of each 16-lane group element i % 4 of the
-// 8-byte chunks addressed by lanes 4j + i / 4 of that group (j = 0..3), so
-// lane r of a group addresses row r0 + r / 4, column col0 + 16 * half + 4 * (r % 4).
-__device__ __forceinline__ void ld_col8(Frag<__bf16>& f, const char* tile, int rs, int r0, int col0,
-                                        int lane) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+// permuted key order of the score accumulators), column 32 j + (lane & 31)
+// for fragment j < NF.  ds_read_b64_tr_b16 gives lane i of each 16-lane group
+// element i % 4 of the 8-byte chunks addressed by lanes 4k + i / 4 of that
+// group (k = 0..3), so lane r of a group addresses row r0 + r / 4, column
+// 32 j + 16 * half + 4 * (r % 4).
+// Before a transposed read of its own the compiler waits for every copy in
+// flight to LDS (it cannot tell the tile read from the tiles those copies
+// fill), which exposes the next tile's copy wherever a tile's copy is still
+// in flight at its first transposed read.  kAsm issues all the reads from one
+// block of inline assembly instead, which is not tied to the copies and waits
+// for its own reads before it ends (so no destination register is handed
+// back before its data has arrived); the price is that the block's reads
+// cannot overlap the work around it.
+template <int NF, bool kAsm>
+__device__ __forceinline__ void ld_col8_row(Frag<__bf16> (&f)[NF], const char* tile, int rs, int r0,
+                                            int lane) {
+  static_assert(NF == 2 || NF == 4, "fragments per row");
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   const int g = lane & 15;
-  const char* p = tile + (r0 + (g >> 2)) * rs + (col0 + 16 * ((lane >> 4) & 1) + 4 * (g & 3)) * 2;
-  const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-  const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * rs));
-  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (!kAsm) {
+    typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const char* p = tile + (r0 + (g >> 2)) * rs + (32 * j + 16 * ((lane >> 4) & 1) + 4 * (g & 3)) * 2;
+      const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+      const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * rs));
+      f[j].v = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    return;
+  }
+  const uint32_t a0 = (uint32_t)reinterpret_cast<uintptr_t>(tile) + (uint32_t)((r0 + (g >> 2)) * rs) +
+                      (uint32_t)((16 * ((lane >> 4) & 1) + 4 * (g & 3)) * 2);
+  const uint32_t a1 = a0 + (uint32_t)(8 * rs);
+  u32x2 x[2 * NF];
+  if constexpr (NF == 4) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:64\n\t"
+        "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:128\n\t"
+        "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+        "ds_read_b64_tr_b16 %7, %9 offset:192\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]),
+          "=&v"(x[7])
+        : "v"(a0), "v"(a1)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:64\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:64\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+        : "v"(a0), "v"(a1)
+        : "memory");
+  }
+#pragma unroll
+  for (int j = 0; j < NF; ++j) {
+    const bf16x4 lo = __builtin_bit_cast(bf16x4, x[2 * j]), hi = __builtin_bit_cast(bf16x4, x[2 * j + 1]);
+    f[j].v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
 }
-__device__ __forceinline__ float frag_get(const Frag<__bf16>& f, int j) { return (float)f.v[j]; }
-__device__ __forceinline__ float frag_get(const Frag<float>& f, int j) { return j < 4 ? f.a[j] : f.b[j - 4]; }
 // accumulator registers r[0..7] -> operand fragment
 __device__ __forceinline__ void from_acc(Frag<__bf16>& f, const f32x16& acc, int base) {
 #pragma unroll
@@ -222,17 +268,6 @@ __device__ __forceinline__ float half_swap_max(float x) {
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
-// OR over each 32-lane half of the wave: returns the half-0 result in the low
-// and the half-1 result in the high 32 bits (wave-uniform).
-__device__ __forceinline__ unsigned long long half_or_dpp(uint32_t v) {
-  v |= dpp_u<0xB1>(v);
-  v |= dpp_u<0x4E>(v);
-  v |= dpp_u<0x141>(v);
-  v |= dpp_u<0x140>(v);
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0) | (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 32) | (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return (unsigned long long)a | ((unsigned long long)b << 32);
 }
 
 // ------------------------------------------------------ entmax powers ---
@@ -464,15 +499,15 @@ struct DirectTile {
       voff[i] = r * RB + ((slot ^ (r & (CPR - 1))) << 4);
     }
   }
-  // load key/value rows row0 .. row0+63 into `tile`
+  // load key/value rows row0 .. row0+63 into `tile` (the LDS offset is the
+  // low 32 bits of the pointer)
   __device__ __forceinline__ void issue(char* tile, int row0, int w) const {
+    const uint32_t d0 = (uint32_t)reinterpret_cast<uintptr_t>(tile);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsrc,
-          reinterpret_cast<__attribute__((address_space(3))) void*>(
-              reinterpret_cast<uintptr_t>(tile + (w * NI + i) * 1024)),
-          16, voff[i], row0 * RB, 0, 0);
+          rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(d0 + (uint32_t)((w * NI + i) * 1024)), 16,
+          voff[i], row0 * RB, 0, 0);
   }
   // address of chunk c (8 elements) of row r
   __device__ __forceinline__ static const __bf16* at(const char* tile, int r, int c) {
@@ -979,17 +1014,18 @@ __device__ __forceinline__ void pv_tile(f32x16 (&oacc)[D / 32], const char* kl, 
       Frag<E> pf;
       from_acc(pf, acc[kb], 8 * s);
       const int koff = 32 * kb + 16 * s + 4 * h;
+      Frag<E> vf[D / 32];
+      if constexpr (kTr) {
+        ld_col8_row<D / 32, false>(vf, vl, VS, koff, lane);
+      } else {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        Frag<E> vf;
-        if constexpr (kTr) {
-          ld_col8(vf, vl, VS, koff, 32 * db, lane);
-        } else {
+        for (int db = 0; db < D / 32; ++db) {
           const E* vrow = reinterpret_cast<const E*>(vl + (32 * db + c32) * VS);
-          ld4x2(vf, vrow + koff, vrow + koff + 8);
+          ld4x2(vf[db], vrow + koff, vrow + koff + 8);
         }
-        mma(oacc[db], vf, pf);
       }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) mma(oacc[db], vf[db], pf);
     }
   }
 }
@@ -1036,27 +1072,49 @@ __device__ __forceinline__ float model_pow(float z, float beta, float& deriv) {
 
 // ------------------------------------------------- histogram start ---
 // A row's histogram over the bracket [lo, hi]: BINS uniform bins of
-// y = x - lo, per bin two 64-bit words of integer moments in units of
-// 2^-hshift (count << 40 plus sum Y, and sum Y^2; see hist_add).  From it:
-// tau's bin, a start value inside it and, for alpha in {1.5, 2} (where f is
-// exact at the bin edges), the bracket narrowed to that bin.  The pages give
-// only "a coarse histogram kept on chip" ("AdaSplash-2: The Transformer
-// Revolution We Didn't See Coming", "Sparse Attention Makes Waves"); the bin
-// count, the moments and the two-point start model are this library's.
-__device__ __forceinline__ void hist_add(unsigned long long* hr, float y, float bin_scale, float ysc,
-                                         unsigned ymax, int bins) {
-  if (y > 0.0f) {
-    const unsigned Y = min((unsigned)(fminf(y, 1.0f) * ysc), ymax);
-    const int b = min((int)(y * bin_scale), bins - 1);
-    atomicAdd(&hr[2 * b], (1ull << 40) + (unsigned long long)Y);
-    atomicAdd(&hr[2 * b + 1], (unsigned long long)Y * (unsigned long long)Y);
+// y = x - lo, per bin two 64-bit words of integer moments of the fixed-point
+// Y = floor(y (2^S - 1)) with S = hshift (count << 40 plus sum Y, and
+// sum Y^2; see hist_add).  From it: tau's bin, a start value inside it and,
+// for alpha in {1.5, 2} (where f is exact at the bin edges), the bracket
+// narrowed to that bin.  The pages give only "a coarse histogram kept on
+// chip" ("AdaSplash-2: The Transformer Revolution We Didn't See Coming",
+// "Sparse Attention Makes Waves"); the bin count, the moments and the
+// two-point start model are this library's.
+//
+// hist_add takes yc = y clamped to [0, 1] (0 drops the entry) and the LDS
+// address of the row's histogram.  With 0 < yc <= 1 and ysc = 2^S - 1
+// (S <= 24) the product rounds to at most 2^S - 1, so Y needs no clamp and
+// Y^2 comes from the two 24-bit multiplies.  kAsm issues the two atomics by
+// inline assembly: the compiler cannot tell the histogram from the tiles
+// that copies in flight fill, and would wait for every copy before an atomic
+// it emits itself.  (The histogram is disjoint from every copy destination;
+// a wave's LDS operations execute in order, and the caller waits for them
+// before the histogram is read.)
+template <bool kAsm>
+__device__ __forceinline__ void hist_add(uint32_t hrow, unsigned long long* hr, float yc, float bin_scale,
+                                         float ysc, int bins) {
+  if (yc > 0.0f) {
+    const unsigned Y = (unsigned)(yc * ysc);
+    __builtin_assume(Y < (1u << 24));
+    const int b = min((int)(yc * bin_scale), bins - 1);
+    const unsigned long long w1 = (1ull << 40) + Y;
+    const unsigned long long w2 = (unsigned long long)Y * (unsigned long long)Y;
+    if constexpr (kAsm) {
+      const uint32_t a = hrow + 16u * (uint32_t)b;
+      asm volatile("ds_add_u64 %0, %1\n\tds_add_u64 %0, %2 offset:8" ::"v"(a), "v"(w1), "v"(w2) : "memory");
+    } else {
+      atomicAdd(&hr[2 * b], w1);
+      atomicAdd(&hr[2 * b + 1], w2);
+    }
   }
 }
+// wait for this wave's LDS operations, those issued by inline assembly included
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int AK, int BINS>
 __device__ __forceinline__ void hist_start(const unsigned long long* hr, float width, float xmax, int hshift,
                                         float beta, float& lo, float& hi, float& tau) {
-  const double yunit = ldexp(1.0, -hshift), yunit2 = yunit * yunit;   // fixed-point units
+  const double yunit = 1.0 / (double)((1u << hshift) - 1u), yunit2 = yunit * yunit;   // fixed-point units
   const double bw = (double)width / BINS;     // bin width in y = x - lo
   const bool exact = (AK == AK15 || AK == AK20);
   double C = 0, S1 = 0, S2 = 0;       // moments of the bins above the edge under test
@@ -1214,6 +1272,57 @@ __device__ __forceinline__ void hist_start(const unsigned long long* hr, float w
 // 32-key halves of active tiles u32[2][4][n_words].
 constexpr int kChunk = 512;    // key tiles listed at once
 
+// One refinement step of a row's tau from the sums of a sweep at tau
+// (F0 = sum t^beta, F1 = sum t^(beta-1), F2 = sum t^(beta-2) or the support
+// count), Halley-bisection or bisection ("Sparse Attention Makes Waves",
+// accelerated alpha-entmax; AdaSplash paper abstract): stop when f is within
+// tolerance or machine precision, else shrink the bracket with the sign of f
+// and take the Halley (or Newton) step when it stays inside it, the midpoint
+// otherwise.  A converged row keeps the tau it was evaluated at.
+template <int AK>
+__device__ __forceinline__ void tau_step(float F0, float F1, float F2, float beta_f, int mode, float tol,
+                                         int max_iters, float& lo, float& hi, float& tau, bool& conv, int& iters) {
+  if (conv) return;
+  ++iters;
+  const double beta = (double)beta_f;
+  const double f = (double)F0 - 1.0;
+  // tau is a float: one ulp of tau moves f by about |f'| ulp, so |f| below
+  // that granularity (or a Halley step below two ulps) is machine precision.
+  const double ulp = (double)FLT_EPSILON * fmax(1.0, fabs((double)tau));
+  const double fp = -beta * (double)F1;
+  const bool bisect = mode == EA_TAU_BISECT;
+  if (fabs(f) <= (double)tol + (bisect ? 0.0 : 2.0 * fabs(fp) * ulp)) {
+    conv = true;
+    return;
+  }
+  if (f > 0.0) lo = tau; else hi = tau;
+  const float wtol = bisect ? 1e-6f * fmaxf(1.0f, fabsf(tau)) : 4.0f * (float)ulp;
+  if (hi - lo <= wtol || iters >= max_iters) {
+    conv = true;
+    return;
+  }
+  double next = 0.5 * ((double)lo + (double)hi);
+  if (!bisect) {
+    // Halley while |f f''| < f'^2; there the step lies between 2/3 and
+    // 2 Newton steps, so a step of two ulps means |f| within three ulps
+    // of |f'|.  Otherwise (for 1.5 < alpha < 2, f'' grows without bound
+    // as a score nears tau from above) a Newton step.
+    const double fpp = (AK == AK20) ? 0.0 : beta * (beta - 1.0) * (double)F2;
+    const bool halley = fabs(f * fpp) < fp * fp;
+    const double th = halley ? (double)tau - 2.0 * f * fp / (2.0 * fp * fp - f * fpp)
+                             : (double)tau - f / fp;
+    if (fabs(th - (double)tau) <= 2.0 * ulp) {
+      conv = true;                        // converged: keep the evaluated tau
+      return;
+    }
+    if (th > (double)lo && th < (double)hi) next = th;
+  }
+  float nt = (float)next;
+  if (!(nt > lo && nt < hi)) nt = lo + 0.5f * (hi - lo);
+  if (!(nt > lo && nt < hi)) conv = true;   // bracket exhausted in float
+  else tau = nt;
+}
+
 template <typename E, int D>
 constexpr int tau_region_bytes(int bins) {
   // histogram [128][2 bins + 2] u64; for bf16 also the V double buffer of the
@@ -1291,7 +1400,6 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   }
   bool conv = !valid;
   int iters = 0;
-  const double beta = (double)P.beta;
 
   // ---- candidate key tiles: bit kt of wave w is set when the block code of
   // tile kt admits a score above some row's lower bracket end (tau >= lo, so
@@ -1342,8 +1450,8 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     // beyond (the host chooses S from N).
     const float width = valid ? fmaxf(hi - lo, 1e-30f) : 1.0f;
     const float bin_scale = (float)BINS / width;
-    const float ysc = (float)(1u << P.hshift);
-    const unsigned ymax = (1u << P.hshift) - 1u;
+    const float ysc = (float)((1u << P.hshift) - 1u);
+    const uint32_t hrow = (uint32_t)reinterpret_cast<uintptr_t>(hr);
     for (int base = 0; base < kt_end; base += kChunk) {
       const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
       RowTiles<E, D, kBK> st(Kh, N, w, lane);
@@ -1364,7 +1472,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
               for (int j = 0; j < 16; ++j) {
-                hist_add(hr, fmaf(acc[kb][j], P.scale, -lo), bin_scale, ysc, ymax, BINS);
+                hist_add<true>(hrow, hr, clamp01(fmaf(acc[kb][j], P.scale, -lo)), bin_scale, ysc, BINS);
               }
           };
           if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
@@ -1376,6 +1484,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         __syncthreads();
       }
     }
+    wait_lds();
     if (valid) hist_start<AK, BINS>(hr, width, xmax, P.hshift, P.beta, lo, hi, tau);
     // the histogram narrowed lo to tau's bin: prune the candidates again
     if (AK == AK15 || AK == AK20) make_cand(std::false_type{});
@@ -1458,10 +1567,11 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     // f, f', f'' terms of key tile kt (staged at kl) and its mask bits
     auto sweep_tile = [&](int kt, const char* kl) {
       auto body = [&](auto masked) {
+        const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
         f32x16 acc[2];
-        tile_scores<E, D>(acc, kl, KS, qf, lane, row_limit(kt * kBK, iq, N, P.causal, h), masked);
         float cnt_at[3];
         cnt_at[0] = Ent<AK>::count(F0, F1, F2, cnt);
+        tile_scores<E, D>(acc, kl, KS, qf, lane, lim, masked);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -1544,47 +1654,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     F0 += __shfl_xor(F0, 32);
     F1 += __shfl_xor(F1, 32);
     F2 += __shfl_xor(F2, 32);
-    if (!conv) {
-      ++iters;
-      const double f = (double)F0 - 1.0;
-      // tau is a float: one ulp of tau moves f by about |f'| ulp, so |f| below
-      // that granularity (or a Halley step below two ulps) is machine precision.
-      const double ulp = (double)FLT_EPSILON * fmax(1.0, fabs((double)tau));
-      const double fp = -beta * (double)F1;
-      const bool bisect = P.mode == EA_TAU_BISECT;
-      if (fabs(f) <= (double)P.tol + (bisect ? 0.0 : 2.0 * fabs(fp) * ulp)) {
-        conv = true;
-      } else {
-        if (f > 0.0) lo = tau; else hi = tau;
-        const float wtol = bisect ? 1e-6f * fmaxf(1.0f, fabsf(tau)) : 4.0f * (float)ulp;
-        if (hi - lo <= wtol || iters >= max_iters) {
-          conv = true;
-        } else {
-          double next = 0.5 * ((double)lo + (double)hi);
-          if (!bisect) {
-            // Halley while |f f''| < f'^2; there the step lies between 2/3 and
-            // 2 Newton steps, so a step of two ulps means |f| within three ulps
-            // of |f'|.  Otherwise (for 1.5 < alpha < 2, f'' grows without bound
-            // as a score nears tau from above) a Newton step.
-            const double fpp = (AK == AK20) ? 0.0 : beta * (beta - 1.0) * (double)F2;
-            const bool halley = fabs(f * fpp) < fp * fp;
-            const double th = halley ? (double)tau - 2.0 * f * fp / (2.0 * fp * fp - f * fpp)
-                                     : (double)tau - f / fp;
-            if (fabs(th - (double)tau) <= 2.0 * ulp) {
-              conv = true;                        // converged: keep the evaluated tau
-            } else if (th > (double)lo && th < (double)hi) {
-              next = th;
-            }
-          }
-          if (!conv) {
-            float nt = (float)next;
-            if (!(nt > lo && nt < hi)) nt = lo + 0.5f * (hi - lo);
-            if (!(nt > lo && nt < hi)) conv = true;   // bracket exhausted in float
-            else tau = nt;
-          }
-        }
-      }
-    }
+    tau_step<AK>(F0, F1, F2, P.beta, P.mode, P.tol, max_iters, lo, hi, tau, conv, iters);
     // Candidates of the next sweep: tau only moves up from lo, so a tile with
     // no score above the lo this sweep used stays empty for every row; a wave
     // whose rows have all converged needs none.  (Only this wave's bits are
@@ -1911,17 +1981,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                   Frag<E> sf, sl;
                   split_acc(sf, sl, sacc, 8 * s);
                   const int koff = 32 * kb + 16 * s + 4 * h;
+                  Frag<E> kf[D / 32];
+                  if constexpr (kTr) {
+                    ld_col8_row<D / 32, true>(kf, kl, KS, koff, lane);
+                  } else {
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                      const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
+                      ld4x2(kf[db], krow + koff, krow + koff + 8);
+                    }
+                  }
 #pragma unroll
                   for (int db = 0; db < D / 32; ++db) {
-                    Frag<E> kf;
-                    if constexpr (kTr) {
-                      ld_col8(kf, kl, KS, koff, 32 * db, lane);
-                    } else {
-                      const E* krow = reinterpret_cast<const E*>(tl + (32 * db + c32) * VS);
-                      ld4x2(kf, krow + koff, krow + koff + 8);
-                    }
-                    mma(gacc[db], kf, sf);
-                    if constexpr (kNeedsLo<E>) mma(gacc[db], kf, sl);
+                    mma(gacc[db], kf[db], sf);
+                    if constexpr (kNeedsLo<E>) mma(gacc[db], kf[db], sl);
                   }
                 }
               }
@@ -2203,21 +2276,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
           from_acc(pf, sacc, 8 * s);
           split_acc(sf, sl, pacc, 8 * s);
           const int qoff = 16 * s + 4 * h;
+          Frag<E> ob[D / 32], qb[D / 32];
+          if constexpr (kTr) {
+            ld_col8_row<D / 32, false>(ob, otl, KS, qoff, lane);
+            ld_col8_row<D / 32, false>(qb, qtl, KS, qoff, lane);
+          } else {
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            Frag<E> ob, qb;
-            if constexpr (kTr) {
-              ld_col8(ob, otl, KS, qoff, 32 * db, lane);
-              ld_col8(qb, qtl, KS, qoff, 32 * db, lane);
-            } else {
+            for (int db = 0; db < D / 32; ++db) {
               const E* orow = reinterpret_cast<const E*>(ottl + (32 * db + c32) * TS);
               const E* qrow = reinterpret_cast<const E*>(qttl + (32 * db + c32) * TS);
-              ld4x2(ob, orow + qoff, orow + qoff + 8);
-              ld4x2(qb, qrow + qoff, qrow + qoff + 8);
+              ld4x2(ob[db], orow + qoff, orow + qoff + 8);
+              ld4x2(qb[db], qrow + qoff, qrow + qoff + 8);
             }
-            mma(dva[db], pf, ob);
-            mma(dka[db], sf, qb);
-            if constexpr (kNeedsLo<E>) mma(dka[db], sl, qb);
+          }
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            mma(dva[db], pf, ob[db]);
+            mma(dka[db], sf, qb[db]);
+            if constexpr (kNeedsLo<E>) mma(dka[db], sl, qb[db]);
           }
         }
       }
@@ -2326,7 +2402,6 @@ __global__ __launch_bounds__(kThreads) void k_entmax_rows(const EI* __restrict__
   const bool vec = P.vec != 0;
   const int n_chunks = (n + 255) / 256;      // chunks of 256 elements (4 per lane)
   unsigned long long* hr = hist_all[w];
-  const double beta = (double)P.beta;
 
   for (long long r = (long long)blockIdx.x * kWaves + w; r < P.rows; r += (long long)gridDim.x * kWaves) {
     const EI* row = S + r * n;
@@ -2375,11 +2450,10 @@ __global__ __launch_bounds__(kThreads) void k_entmax_rows(const EI* __restrict__
       __builtin_amdgcn_wave_barrier();
       const float width = fmaxf(hi - lo, 1e-30f);
       const float bin_scale = (float)kRowBins / width;
-      const float ysc = (float)(1u << P.hshift);
-      const unsigned ymax = (1u << P.hshift) - 1u;
+      const float ysc = (float)((1u << P.hshift) - 1u);
       for_chunks([&](const f32x4& v, int) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hist_add(hr, v[i] - lo, bin_scale, ysc, ymax, kRowBins);
+        for (int i = 0; i < 4; ++i) hist_add<false>(0u, hr, clamp01(v[i] - lo), bin_scale, ysc, kRowBins);
       });
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -2401,27 +2475,7 @@ __global__ __launch_bounds__(kThreads) void k_entmax_rows(const EI* __restrict__
       F0 = wave_sum(F0);
       F1 = wave_sum(F1);
       if (P.mode != EA_TAU_BISECT && AK != AK20) F2 = wave_sum(F2);
-      ++iters;
-      const double f = (double)F0 - 1.0;
-      const double ulp = (double)FLT_EPSILON * fmax(1.0, fabs((double)tau));
-      const double fp = -beta * (double)F1;
-      const bool bisect = P.mode == EA_TAU_BISECT;
-      if (fabs(f) <= (double)P.tol + (bisect ? 0.0 : 2.0 * fabs(fp) * ulp)) break;
-      if (f > 0.0) lo = tau; else hi = tau;
-      const float wtol = bisect ? 1e-6f * fmaxf(1.0f, fabsf(tau)) : 4.0f * (float)ulp;
-      if (hi - lo <= wtol || iters >= P.max_iters) break;
-      double next = 0.5 * ((double)lo + (double)hi);
-      if (!bisect) {
-        const double fpp = (AK == AK20) ? 0.0 : beta * (beta - 1.0) * (double)F2;
-        const bool halley = fabs(f * fpp) < fp * fp;
-        const double th = halley ? (double)tau - 2.0 * f * fp / (2.0 * fp * fp - f * fpp) : (double)tau - f / fp;
-        if (fabs(th - (double)tau) <= 2.0 * ulp) break;
-        if (th > (double)lo && th < (double)hi) next = th;
-      }
-      float nt = (float)next;
-      if (!(nt > lo && nt < hi)) nt = lo + 0.5f * (hi - lo);
-      if (!(nt > lo && nt < hi)) break;
-      tau = nt;
+      tau_step<AK>(F0, F1, F2, P.beta, P.mode, P.tol, P.max_iters, lo, hi, tau, conv, iters);
     }
     // probabilities at the final tau
     EO* prow = Pout + r * n;

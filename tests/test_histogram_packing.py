@@ -1,7 +1,7 @@
 """Host model of the tau kernel's histogram packing (CPU only).
 
 Per row and bin the kernel keeps two 64-bit words of integer moments of
-y = x - lo in fixed point Y = min(floor(min(y, 1) 2^S), 2^S - 1):
+y = x - lo in fixed point Y = floor(min(y, 1) (2^S - 1)) (so Y < 2^S):
     word 1 = (count << 40) + sum Y,     word 2 = sum Y^2    (both mod 2^64),
 and for alpha = 1.5 reads f exactly at every bin edge e from the moments of
 the bins above it: f(e) = S2 - 2 e S1 + e^2 C - 1.  tau's bin is the highest
@@ -35,7 +35,7 @@ def packed_bins(y, width, S):
     for yy in y:
         if yy <= 0.0:
             continue
-        Y = min(int(math.floor(min(yy, 1.0) * (1 << S))), (1 << S) - 1)
+        Y = int(math.floor(min(yy, 1.0) * ((1 << S) - 1)))
         b = min(int(yy * BINS / width), BINS - 1)
         w1[b] = (w1[b] + (1 << 40) + Y) & M64
         w2[b] = (w2[b] + Y * Y) & M64
@@ -44,7 +44,7 @@ def packed_bins(y, width, S):
 
 def tau_bin(w1, w2, width, S):
     """Highest bin b whose lower edge has f >= 0 (f exact at the edges)."""
-    u = 2.0 ** -S
+    u = 1.0 / ((1 << S) - 1)
     C = S1 = S2 = 0.0
     for b in range(BINS - 1, -1, -1):
         C += w1[b] >> 40
@@ -69,7 +69,7 @@ def test_shift_rule_never_overflows():
 def test_tied_bin_overflow_and_fix():
     """150000 tied scores just above the lower edge of bin 14 plus ten at the
     row maximum (alpha = 1.5).  The exact tau (sort-based oracle) lies in
-    bin 13; the old 2^-24 packing overflows and picks another bin, the packing
+    bin 13; a packing with S = 24 overflows and picks another bin, the packing
     with the library's shift picks bin 13."""
     n_tie, n_top = 150000, 10
     n = n_tie + n_top
@@ -80,8 +80,8 @@ def test_tied_bin_overflow_and_fix():
     tau = O.tau_sort(x, 1.5)[0]
     true_bin = int((tau + 1.0) * BINS / width)
     assert true_bin == 13
-    old = tau_bin(*packed_bins(y, width, 24), width, 24)
-    assert old != true_bin                    # the overflow this packing had
+    wrapped = tau_bin(*packed_bins(y, width, 24), width, 24)
+    assert wrapped != true_bin                # S = 24 overflows at this n
     S = shift_rule(n)
     assert S == 22
     assert tau_bin(*packed_bins(y, width, S), width, S) == true_bin
