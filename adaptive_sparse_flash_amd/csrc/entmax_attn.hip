@@ -881,21 +881,44 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
                 kt_end);
     float m = -INFINITY;
 
-    auto tile = [&](int s, int kt, auto masked) -> float {
-      const char* kl = smem + (s % (2 * TPS)) * DT::BYTES;
-      f32x4 acc[4][4];               // [query block][key block]
+    // scores of the tile staged at kl into acc[query block][key block]; the
+    // four A fragments of step ks + 1 are read while step ks's sixteen MFMAs
+    // run, so no MFMA waits for an LDS read
+    auto mfma_tile = [&](f32x4 (&acc)[4][4], const char* kl) {
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) acc[b][kb] = f32x4{0, 0, 0, 0};
+      bf16x8 a[2][4];
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks)
+      for (int kb = 0; kb < 4; ++kb) a[0][kb] = *reinterpret_cast<const bf16x8*>(DT::at(kl, 16 * kb + c16, g));
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(DT::at(kl, 16 * kb + c16, 4 * ks + g));
+      for (int ks = 0; ks < KST; ++ks) {
+        if (ks + 1 < KST) {
 #pragma unroll
-          for (int b = 0; b < 4; ++b) acc[b][kb] = mma16(a, qf[b][ks], acc[b][kb]);
+          for (int kb = 0; kb < 4; ++kb)
+            a[(ks + 1) & 1][kb] = *reinterpret_cast<const bf16x8*>(DT::at(kl, 16 * kb + c16, 4 * (ks + 1) + g));
         }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[b][kb] = mma16(a[ks & 1][kb], qf[b][ks], acc[b][kb]);
+      }
+    };
+    // the schedule of one mfma_tile (a hint to the scheduler, which otherwise
+    // moves the reads back next to their MFMAs): its first step's reads, then
+    // each fragment's four MFMAs followed by one read of the next step
+    auto sched_tile = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // DS reads
+#pragma unroll
+      for (int i = 0; i < 4 * KST; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0); // MFMAs
+        if (i < 4 * (KST - 1)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    };
+    // the tile's maximum for each query (after masking), the running row
+    // maximum m and the block's value for the tile code
+    auto epilogue = [&](f32x4 (&acc)[4][4], int kt, auto masked) -> float {
       if constexpr (decltype(masked)::value) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -930,6 +953,12 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
       const float tm = fmax_nan(__uint_as_float(s01[0]), __uint_as_float(s01[1]));
       m = fmaxf(m, tm);
       return half_max32(tm == -INFINITY ? -INFINITY : (tm - m) * P.scale);
+    };
+    auto tile = [&](int s, int kt, auto masked) -> float {
+      f32x4 acc[4][4];
+      mfma_tile(acc, smem + (s % (2 * TPS)) * DT::BYTES);
+      sched_tile();
+      return epilogue(acc, kt, masked);
     };
 
     // Step over TPS tiles: wait for them (issued one step earlier; this also
