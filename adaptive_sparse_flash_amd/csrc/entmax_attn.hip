@@ -482,12 +482,12 @@ struct RowStage {
 // that read the same chunk of 16 consecutive rows hit 16 different bank
 // groups.  The buffer descriptor spans one head's N rows: rows past N read as
 // zeros (the hardware range check), and every reader masks them.
-template <int D>
+template <int D, int W = kWaves>
 struct DirectTile {
   static constexpr int RB = D * 2;                 // row bytes
   static constexpr int CPR = RB / 16;              // chunks per row
   static constexpr int BYTES = kBK * RB;
-  static constexpr int NI = BYTES / 1024 / kWaves; // instructions per wave
+  static constexpr int NI = BYTES / 1024 / W;      // instructions per wave (W waves share a tile)
   __amdgpu_buffer_rsrc_t rsrc;
   int voff[NI];                                    // this lane's byte offsets in a tile
   __device__ __forceinline__ DirectTile(const __bf16* head, int N, int w, int lane) {
@@ -827,19 +827,21 @@ __device__ __forceinline__ f32x4 mma16(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 constexpr int kRowmaxTPS = 2;      // K tiles per barrier step (two steps of slots in LDS)
+constexpr int kRowmaxWaves = kWaves;           // waves per workgroup, 64 queries each
+constexpr int kRowmaxQ = 64 * kRowmaxWaves;     // queries per workgroup
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict__ Q,
-                                                       const __bf16* __restrict__ K, Params P,
-                                                       float* __restrict__ rowmax,
-                                                       uint8_t* __restrict__ blkc) {
+__global__ __launch_bounds__(64 * kRowmaxWaves) void k_rowmax16(const __bf16* __restrict__ Q,
+                                                                const __bf16* __restrict__ K, Params P,
+                                                                float* __restrict__ rowmax,
+                                                                uint8_t* __restrict__ blkc) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  using DT = DirectTile<D>;
+  using DT = DirectTile<D, kRowmaxWaves>;
   constexpr int TPS = kRowmaxTPS;
   constexpr int KST = D / 32;      // contraction steps of 32
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
   const int N = P.N;
-  const int n_qt = (N + 255) / 256;
-  // Causal query tile t holds 4 (t + 1) key tiles of work.  With pair_qt a
+  const int n_qt = (N + kRowmaxQ - 1) / kRowmaxQ;
+  // Causal query tile t holds (kRowmaxQ / 64) (t + 1) key tiles of work.  With pair_qt a
   // workgroup takes the pair (n_qt - 1 - t, t), so that every workgroup
   // sweeps the same number of tiles (the middle tile of an odd count runs
   // alone); otherwise one tile per workgroup, heaviest first.
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
   const int ktc = blk_row(P.n_kt);
 
   auto sweep = [&](int qtile) {
-    const int q0 = qtile * 256;
+    const int q0 = qtile * kRowmaxQ;
     const int wq0 = q0 + 64 * w;
     // B fragments: query wq0 + 16 b + c16, dimensions 32 ks + 8 g ... + 7
     bf16x8 qf[4][KST];
@@ -863,7 +865,7 @@ __global__ __launch_bounds__(kThreads) void k_rowmax16(const __bf16* __restrict_
         qf[b][ks] = qi < N ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)qi * D + 32 * ks + 8 * g)
                            : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    const int kt_end = P.causal ? (min(N - 1, q0 + 255) / kBK + 1) : P.n_kt;
+    const int kt_end = P.causal ? (min(N - 1, q0 + kRowmaxQ - 1) / kBK + 1) : P.n_kt;
     const int kt_end_w = wq0 >= N ? 0 : (P.causal ? (min(N - 1, wq0 + 63) / kBK + 1) : P.n_kt);
     const int kt_full = min(P.causal ? q0 / kBK : P.n_kt, N / kBK);
     const int n_diag = kt_end - kt_full;
@@ -2703,7 +2705,8 @@ bool pair_query_tiles(const Shape& s, int causal) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return false;
-  const long tiles = (long)s.n_qt256 * s.BH, slots = 2L * cus;
+  // resident row-max workgroups: two waves per SIMD, 64 queries per wave
+  const long tiles = (long)((s.N + kRowmaxQ - 1) / kRowmaxQ) * s.BH, slots = 8L * cus / kRowmaxWaves;
   return 2 * tiles > 3 * slots && 2 * tiles <= 5 * slots;
 }
 
@@ -2785,8 +2788,9 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   tm.begin(EA_STAGE_ROWMAX);
   if constexpr (kTr) {
     P.pair_qt = pair_query_tiles(s, P.causal) ? 1 : 0;
-    const int units = P.pair_qt ? (s.n_qt256 + 1) / 2 : s.n_qt256;
-    rc = launch(k_rowmax16<D>, dim3(units * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, blkc);
+    const int n_qt = (s.N + kRowmaxQ - 1) / kRowmaxQ;
+    const int units = P.pair_qt ? (n_qt + 1) / 2 : n_qt;
+    rc = launch(k_rowmax16<D>, dim3(units * s.BH), dim3(64 * kRowmaxWaves), rm_lds, st, Q, K, P, rowmax, blkc);
   } else {
     rc = launch(k_rowmax<E, D>, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, blkc);
   }
