@@ -29,13 +29,15 @@
 //    clamp modifier: tau >= max(x) - 1 keeps every t <= 1.
 //  * The first sweep (k_rowmax16 for bf16: 16x16x32 MFMA, sixteen independent
 //    accumulators per wave, K tiles loaded straight into XOR-swizzled LDS)
-//    takes only row maxima and each row's maximum over every 64-key tile.
-//    Tiles whose maximum cannot exceed a row's lower bracket end can never
-//    hold a nonzero probability, so the histogram and Halley sweeps visit
-//    candidate tiles only; the tile maxima also raise the lower bracket end.
+//    takes only row maxima and, per 32-query block and 64-key tile, a one-byte
+//    code bounding the block's largest score in that tile below the rows'
+//    maxima.  Tiles whose code rules out any score above a row's lower
+//    bracket end can never hold a nonzero probability, so the histogram and
+//    Halley sweeps visit candidate tiles only.
 //  * The histogram holds integer moments (count, sum y, sum y^2 of
-//    y = x - lo in 2^-24 fixed point) updated with LDS integer atomics, so it is
-//    deterministic and, for alpha in {1.5, 2}, gives f exactly at bin edges.
+//    y = x - lo in fixed point, Y = floor(y (2^S - 1)) with S chosen from N)
+//    updated with LDS integer atomics, so it is deterministic and, for alpha
+//    in {1.5, 2}, gives f exactly at bin edges.
 //  * The sparse kernels stage d = 128 bf16 tiles with buffer_load ... lds
 //    (no staging registers) and keep LDS reads several MFMA steps ahead.
 //  * For bf16 the tau kernel ends with the P V pass over its final mask
@@ -1474,7 +1476,7 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   if (P.mode == EA_TAU_HIST_HALLEY) {
     for (int e = threadIdx.x; e < kBQW * HROW; e += kThreads) hist[e] = 0ull;
     unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * HROW;
-    // Bins split [lo, hi]; moments are kept in units of 2^-S of y = x - lo <= 1
+    // Bins split [lo, hi]; moments are kept in units of 1/(2^S - 1) of y = x - lo <= 1
     // with Y <= 2^S - 1: the count sits at bit 40, sum Y below it and sum Y^2
     // in a word of its own, so with at most N <= 2^(40-S) elements per bin
     // sum Y < 2^40 and sum Y^2 < 2^64.  S = 24 up to N = 65536, fewer bits

@@ -100,7 +100,7 @@ typedef struct {
 
 /* Stages, for the timing hook. */
 #define EA_STAGE_FWD_PREP  0   /* forward: V^T copy (fp32 inputs only) */
-#define EA_STAGE_ROWMAX    1   /* forward: the full score sweep (row and tile maxima) */
+#define EA_STAGE_ROWMAX    1   /* forward: the full score sweep (row maxima and block codes) */
 #define EA_STAGE_TAU       2   /* forward: histogram and Halley sweeps over candidate tiles, block mask;
                                   for bf16 inputs also O = P V (one kernel) */
 #define EA_STAGE_PV        3   /* forward: O = P V over active tiles (fp32 inputs; empty for bf16) */
