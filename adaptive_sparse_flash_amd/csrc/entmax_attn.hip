@@ -1144,6 +1144,36 @@ __device__ __forceinline__ void hist_add(uint32_t hrow, unsigned long long* hr, 
 // wait for this wave's LDS operations, those issued by inline assembly included
 __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Bin edges as bracket ends: lo + e, widened by the float rounding of x and
+// lo and by the fixed-point truncation of y (sign -1: a lower end, +1: upper).
+__device__ __forceinline__ float hist_edge(float lo, double e, float xmax, int hshift, float sign) {
+  const double yunit = 1.0 / (double)((1u << hshift) - 1u);
+  const float margin = fmaxf(1.0f, fabsf(xmax)) * 5e-7f + 1e-6f + (float)(2.0 * yunit);
+  return (float)((double)lo + e) + sign * margin;
+}
+
+// alpha in {1.5, 2}: the highest bin whose lower edge has f >= 0, with f
+// taken from the moments of the bins above the edge (0 if no edge above the
+// first qualifies).  Moments of only some of a row's scores give a value
+// below f at every edge, so the edge found is a lower bound on tau even then.
+template <int AK, int BINS>
+__device__ __forceinline__ int hist_floor_bin(const unsigned long long* hr, float width, int hshift) {
+  const double yunit = 1.0 / (double)((1u << hshift) - 1u), yunit2 = yunit * yunit;
+  const double bw = (double)width / BINS;
+  double C = 0, S1 = 0, S2 = 0;
+#pragma unroll 1
+  for (int b = BINS - 1; b > 0; --b) {
+    const unsigned long long h1 = hr[2 * b], h2 = hr[2 * b + 1];
+    C += (double)(h1 >> 40);
+    S1 += (double)(h1 & ((1ull << 40) - 1ull)) * yunit;
+    S2 += (double)h2 * yunit2;
+    const double e = (double)b * bw;
+    const double f = AK == AK15 ? S2 - 2.0 * e * S1 + e * e * C - 1.0 : S1 - e * C - 1.0;
+    if (f >= 0.0) return b;
+  }
+  return 0;
+}
+
 template <int AK, int BINS>
 __device__ __forceinline__ void hist_start(const unsigned long long* hr, float width, float xmax, int hshift,
                                         float beta, float& lo, float& hi, float& tau) {
@@ -1284,10 +1314,8 @@ __device__ __forceinline__ void hist_start(const unsigned long long* hr, float w
   }
   const float t0x = (float)((double)lo + t0);
   if (exact) {
-    // float rounding of x and lo, and the fixed-point truncation of y
-    const float margin = fmaxf(1.0f, fabsf(xmax)) * 5e-7f + 1e-6f + (float)(2.0 * yunit);
-    const float nlo = (float)((double)lo + eb) - margin;
-    const float nhi = (float)((double)lo + eb1) + margin;
+    const float nlo = hist_edge(lo, eb, xmax, hshift, -1.0f);
+    const float nhi = hist_edge(lo, eb1, xmax, hshift, 1.0f);
     if (nlo > lo) lo = nlo;
     if (nhi < hi) hi = nhi;
   }
@@ -1304,6 +1332,10 @@ __device__ __forceinline__ void hist_start(const unsigned long long* hr, float w
 // bits of tiles above the lower bracket end u32[4][n_words] | bits of the two
 // 32-key halves of active tiles u32[2][4][n_words].
 constexpr int kChunk = 512;    // key tiles listed at once
+// the histogram takes two passes when more lanes than this hold candidate
+// tiles outside the strong ones (16 tiles a lane; below it the first pass
+// would save little)
+constexpr int kStrongMinWeak = 8;
 
 // One refinement step of a row's tau from the sums of a sweep at tau
 // (F0 = sum t^beta, F1 = sum t^(beta-1), F2 = sum t^(beta-2) or the support
@@ -1440,13 +1472,20 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
   // compares the code with the smallest lo_i - max_j x_ij of the wave's rows,
   // less a margin for the float rounding of both sides.  Words past the
   // wave's last visible tile are written as zeros up to the workgroup's end.
-  auto make_cand = [&](auto use_pre) {
+  // The first call (use_pre) also leaves each wave's strong tiles in mbits
+  // for the two-pass histogram (below): its candidates with block code 0,
+  // which hold the highest scores of some of its rows.  It returns the
+  // number of the workgroup's lanes that hold other candidates.
+  constexpr bool kStrongAK = AK == AK15 || AK == AK20;
+  const bool strong_pass = kStrongAK && !dense && P.mode == EA_TAU_HIST_HALLEY;
+  auto make_cand = [&](auto use_pre) -> int {
     __syncthreads();   // earlier readers of the bits are done
     // (the MFMA shapes of the row-max sweep and of this kernel round their
     // partial sums differently: 64 float epsilons of |x| covers that)
     float th = valid ? (lo - xmax) - 64.0f * FLT_EPSILON * (fmaxf(1.0f, fabsf(xmax)) + 2.0f) : INFINITY;
     th = half_min32(th);           // both lane halves hold the same 32 rows
     const float lim = -128.0f * th;   // candidate iff code < lim
+    int weak = 0;
     for (int base = 0; base < kt_end; base += 64 * 16) {
       const int t0 = base + 16 * lane;
       u32x4 r = u32x4{~0u, ~0u, ~0u, ~0u};
@@ -1454,11 +1493,14 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
         r = pre;
       else if (t0 < kt_end_w)
         r = *reinterpret_cast<const u32x4*>(crow + t0);
-      uint32_t bits = 0;
+      uint32_t bits = 0, sb = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const uint32_t c = (r[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-        if ((float)c < lim && t0 + j < kt_end_w) bits |= 1u << j;
+        if ((float)c < lim && t0 + j < kt_end_w) {
+          bits |= 1u << j;
+          if (c == 0u) sb |= 1u << j;
+        }
       }
       const int nv = min(max(kt_end_w - t0, 0), 16);
       if (dense) bits = nv >= 16 ? 0xFFFFu : ((1u << nv) - 1u);
@@ -1466,11 +1508,25 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
       const uint32_t word = bits | (dpp_u<0xB1>(bits) << 16);
       const int wd = (base >> 5) + (lane >> 1);
       if (!(lane & 1) && wd < n_words) cbits[w * n_words + wd] = word;
+      if constexpr (decltype(use_pre)::value) {
+        if (strong_pass) {
+          weak |= (bits & ~sb) != 0u;
+          const uint32_t sword = sb | (dpp_u<0xB1>(sb) << 16);
+          if (!(lane & 1) && wd < n_words) mbits[w * n_words + wd] = sword;
+        }
+      }
+    }
+    // (lanes that hold other candidates, per wave, beside build_list's counter)
+    if (decltype(use_pre)::value && strong_pass) {
+      const int nw = __popcll(__ballot(weak));
+      if (lane == 0) counter[4 + w] = nw;
     }
     __syncthreads();
+    if (decltype(use_pre)::value && strong_pass) return counter[4] + counter[5] + counter[6] + counter[7];
+    return 0;
   };
   auto cand = [&](int ww, int kt) -> bool { return (cbits[ww * n_words + (kt >> 5)] >> (kt & 31)) & 1u; };
-  make_cand(std::true_type{});
+  const int weak_lanes = make_cand(std::true_type{});
 
   // ---- histogram initialisation (AdaSplash-2)
   if (P.mode == EA_TAU_HIST_HALLEY) {
@@ -1485,40 +1541,81 @@ __global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const
     const float bin_scale = (float)BINS / width;
     const float ysc = (float)((1u << P.hshift) - 1u);
     const uint32_t hrow = (uint32_t)reinterpret_cast<uintptr_t>(hr);
-    for (int base = 0; base < kt_end; base += kChunk) {
-      const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
-      RowTiles<E, D, kBK> st(Kh, N, w, lane);
-      if (n > 0) {
-        st.fetch(kbuf, (base + list[0]) * kBK);
-        st.commit(kbuf);
-      }
+    const float lo0 = lo;   // the histogram's origin
+    // Histogram passes: 0 takes every candidate tile.  For alpha in {1.5, 2}
+    // there are two instead: pass 1 takes the strong tiles only (each wave's
+    // candidates with block code 0, joined over the workgroup).  f of their
+    // scores alone
+    // lies below f, so their histogram's highest edge with f >= 0 is a lower
+    // bound on tau; it prunes the candidates, and pass 2 adds the remaining
+    // candidates of the raised bound.  Every score above that bound is then
+    // in the histogram, so f at every edge above it, tau's bin, the start and
+    // the narrowed bracket come out as from pass 0; only tiles that cannot
+    // reach the bound are skipped.
+    auto strong = [&](int kt) -> bool { return (lbits[kt >> 5] >> (kt & 31)) & 1u; };
+    // two passes only when the workgroup holds enough other candidates to
+    // skip some of them
+    const bool two = strong_pass && weak_lanes > kStrongMinWeak;
+    if (two) {
+      // the union of the waves' strong tiles, in lbits (first written by the sweeps)
+      for (int e = threadIdx.x; e < n_words; e += kThreads)
+        lbits[e] = mbits[e] | mbits[n_words + e] | mbits[2 * n_words + e] | mbits[3 * n_words + e];
       __syncthreads();
-      for (int i = 0; i < n; ++i) {
-        const int kt = base + list[i];
-        if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
-        if ((wbits[i] >> w) & 1) {
-          auto body = [&](auto masked) {
-            f32x16 acc[2];
-            tile_scores<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane,
-                              row_limit(kt * kBK, iq, N, P.causal, h), masked);
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int j = 0; j < 16; ++j) {
-                hist_add<true>(hrow, hr, clamp01(fmaf(acc[kb][j], P.scale, -lo)), bin_scale, ysc, BINS);
-              }
-          };
-          if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
-            body(std::true_type{});
-          else
-            body(std::false_type{});
+    }
+    const int hp_first = two ? 1 : 0, hp_last = two ? 2 : 0;
+#pragma clang loop unroll(disable)
+    for (int hp = hp_first; hp <= hp_last; ++hp) {
+      if (hp == 2) {
+        wait_lds();
+        if (valid) {
+          const int b = hist_floor_bin<AK, BINS>(hr, width, P.hshift);
+          if (b > 0) lo = fmaxf(lo, hist_edge(lo0, (double)b * ((double)width / BINS), xmax, P.hshift, -1.0f));
         }
-        if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
+        make_cand(std::false_type{});
+      }
+      auto pred = [&](int ww, int kt) -> bool {
+        return cand(ww, kt) && (hp == 0 || (hp == 1) == strong(kt));
+      };
+      for (int base = 0; base < kt_end; base += kChunk) {
+        const int n = build_list(base, min(kChunk, kt_end - base), pred, list, wbits, flags, counter);
+        RowTiles<E, D, kBK> st(Kh, N, w, lane);
+        if (n > 0) {
+          st.fetch(kbuf, (base + list[0]) * kBK);
+          st.commit(kbuf);
+        }
         __syncthreads();
+        for (int i = 0; i < n; ++i) {
+          const int kt = base + list[i];
+          if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
+          if ((wbits[i] >> w) & 1) {
+            auto body = [&](auto masked) {
+              f32x16 acc[2];
+              tile_scores<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane,
+                                row_limit(kt * kBK, iq, N, P.causal, h), masked);
+#pragma unroll
+              for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                  hist_add<true>(hrow, hr, clamp01(fmaf(acc[kb][j], P.scale, -lo0)), bin_scale, ysc, BINS);
+                }
+            };
+            if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+              body(std::true_type{});
+            else
+              body(std::false_type{});
+          }
+          if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
+          __syncthreads();
+        }
       }
     }
     wait_lds();
-    if (valid) hist_start<AK, BINS>(hr, width, xmax, P.hshift, P.beta, lo, hi, tau);
+    if (valid) {
+      float lo_h = lo0;
+      hist_start<AK, BINS>(hr, width, xmax, P.hshift, P.beta, lo_h, hi, tau);
+      lo = fmaxf(lo, lo_h);
+      tau = fminf(fmaxf(tau, lo), hi);
+    }
     // the histogram narrowed lo to tau's bin: prune the candidates again
     if (AK == AK15 || AK == AK20) make_cand(std::false_type{});
   } else if (P.mode == EA_TAU_HALLEY_BISECT) {

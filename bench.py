@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark: fused alpha-entmax attention, forward + backward, on one MI355X.
 
-One step = the whole hot path over one batch: entmax_attn_fwd (row and tile
-maxima, tau solve with block mask, P V) followed by entmax_attn_bwd (delta and
-dQ, then dK/dV), inputs resident in HBM before timing starts.
+One step = the whole hot path over one batch: entmax_attn_fwd (row maxima and
+block codes, tau solve with block mask, P V) followed by entmax_attn_bwd (delta
+and dQ, then dK/dV), inputs resident in HBM before timing starts.  The timed
+steps replay one HIP graph that holds a step's kernels (checked bit for bit
+against an eager step first); the stage times come from a separate eager pass.
 
 Default workload (the one the headline metric is quoted on): B=1, H=16,
 N=16384, d=128, bf16, causal, alpha=1.5, planted-cluster locality (64 random
@@ -225,24 +227,70 @@ class Runner:
         self.bufs.forward(self.q, self.k, self.v, w.alpha, w.causal)
         self.bufs.backward(self.q, self.k, self.v, self.do, w.alpha, w.causal)
 
-    def measure(self, steps, warmup):
+    def capture(self):
+        """One step (forward + backward) captured as a HIP graph, or None if a
+        replay differs from the eager step.  The replays are checked bit for
+        bit against an eager step on zeroed outputs, with eager steps between
+        them."""
+        torch = self.torch
+        b = self.bufs
+        outs = (b.out, b.tau, b.dq, b.dk, b.dv)
+        self.step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        for _ in range(2):
+            for t in outs:
+                t.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(u, v) for u, v in zip(ref, outs)):
+                return None
+            self.step()
+            torch.cuda.synchronize()
+        return g
+
+    def measure(self, steps, warmup, graph=True):
+        """`warmup` eager steps, then exactly `steps` timed steps, each one
+        replay of a HIP graph holding the step's kernels (eager launches if
+        graph is False or the replay check fails).  Stage times come from a
+        separate eager pass with the library's events."""
         torch, A = self.torch, self.A
         ns = A.binding.EA_NUM_STAGES
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        ev = HipEvents(2 * ns * steps)
+        g = self.capture() if graph else None
+        run_step = g.replay if g is not None else self.step
+        launch = "hip_graph" if g is not None else "eager"
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for s in range(steps):
+        for _ in range(steps):
+            run_step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        del g
+        n_ev = max(1, min(steps, 10))
+        ev = HipEvents(2 * ns * n_ev)
+        torch.cuda.synchronize()
+        te0 = time.perf_counter()
+        for s in range(n_ev):
             self.bufs.desc.events = ev.block(s, 2 * ns)
             self.step()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
+        te1 = time.perf_counter()
         self.bufs.desc.events = None
         stage_ms = {}
         for si, name in enumerate(A.binding.STAGES):
-            vals = [ev.elapsed_ms(s * 2 * ns + 2 * si, s * 2 * ns + 2 * si + 1) for s in range(steps)]
+            vals = [ev.elapsed_ms(s * 2 * ns + 2 * si, s * 2 * ns + 2 * si + 1) for s in range(n_ev)]
             stage_ms[name] = float(np.mean(vals))
         ev.close()
         w = self.w
@@ -250,6 +298,8 @@ class Runner:
         iters = self.bufs.iters.cpu().numpy()
         ms = (t1 - t0) / steps * 1e3
         return {"ms_per_step": ms, "tflops": dense_equiv_flops(w) / (ms * 1e-3) / 1e12,
+                "launch": launch,
+                "ms_per_step_eager": (te1 - te0) / n_ev * 1e3,
                 "block_sparsity_32x32": micro_sparsity(mask, w.N, w.causal),
                 "block_sparsity_32x64": block_sparsity(mask, w.N, w.causal, 1),
                 "block_sparsity_128x64": block_sparsity(mask, w.N, w.causal, 4),
@@ -401,6 +451,8 @@ def main():
             "tau_iters_mean": head["tau_iters_mean"],
             "tau_iters_max": head["tau_iters_max"],
             "stage_ms": stage_ms,
+            "launch": head["launch"],
+            "ms_per_step_eager": head["ms_per_step_eager"],
             "workspace_bytes": ws_bytes,
         },
         "roofline": roofline,
