@@ -449,6 +449,41 @@ __device__ __forceinline__ void map_tile(int n_tiles, int BH, bool heavy_first, 
   tile = heavy_first ? n_tiles - 1 - rank : rank;
 }
 
+// Persistent workgroups: a kernel launched with one workgroup per resident
+// slot takes its work units from a queue, in the order map_tile deals them
+// (heavy first when causal), instead of leaving the order to the hardware
+// dispatcher, which holds later workgroups back while earlier ones still run
+// and leaves slots idle when unit lengths vary widely.  With B*H a multiple
+// of 8 there is one queue per XCD, serving that XCD's heads; otherwise one.
+// queue[] holds kQueues counters that the preceding kernel in the same call
+// zeroes.  Every thread gets the unit; false once the queue is empty.
+constexpr int kQueues = 8;
+constexpr int kQueueBytes = 256;
+__device__ __forceinline__ bool next_unit(int* queue, int* s_unit, int n_tiles, int BH, bool heavy_first,
+                                          int& bh, int& tile) {
+  const bool per_xcd = (BH & 7) == 0;
+  const int xq = per_xcd ? (int)(blockIdx.x & 7) : 0;
+  const int n_units = per_xcd ? n_tiles * (BH >> 3) : n_tiles * BH;
+  if (threadIdx.x == 0) *s_unit = atomicAdd(queue + xq, 1);
+  __syncthreads();
+  const int u = __builtin_amdgcn_readfirstlane(*s_unit);   // uniform: the unit's values stay scalar
+  if (u >= n_units) return false;
+  int rank;
+  if (per_xcd) {
+    const int hx = BH >> 3;
+    bh = xq * hx + u % hx;
+    rank = u / hx;
+  } else {
+    bh = u % BH;
+    rank = u / BH;
+  }
+  tile = heavy_first ? n_tiles - 1 - rank : rank;
+  return true;
+}
+__device__ __forceinline__ void reset_queues(int* queue) {
+  if (queue && blockIdx.x == 0 && threadIdx.x < kQueues) queue[threadIdx.x] = 0;
+}
+
 // ---------------------------------------------------- prefetch staging ---
 // A tile of ROWS rows x D elements staged global -> registers -> LDS, so the
 // global loads of the next tile overlap the MFMA work on the current one.
@@ -708,9 +743,10 @@ struct BlkCodes {
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_rowmax(const E* __restrict__ Q, const E* __restrict__ K,
                                                      Params P, float* __restrict__ rowmax,
-                                                     uint8_t* __restrict__ blkc) {
+                                                     uint8_t* __restrict__ blkc, int* __restrict__ queue) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KS = row_stride<E, D>();
+  reset_queues(queue);   // for k_tau, which runs next
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
   const int n_qt = (N + 255) / 256;
@@ -835,9 +871,11 @@ template <int D>
 __global__ __launch_bounds__(64 * kRowmaxWaves) void k_rowmax16(const __bf16* __restrict__ Q,
                                                                 const __bf16* __restrict__ K, Params P,
                                                                 float* __restrict__ rowmax,
-                                                                uint8_t* __restrict__ blkc) {
+                                                                uint8_t* __restrict__ blkc,
+                                                                int* __restrict__ queue) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   using DT = DirectTile<D, kRowmaxWaves>;
+  reset_queues(queue);   // for k_tau, which runs next
   constexpr int TPS = kRowmaxTPS;
   constexpr int KST = D / 32;      // contraction steps of 32
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
@@ -1398,465 +1436,522 @@ constexpr int tau_region_bytes(int bins) {
 }
 
 template <typename E, int D, int AK, int BINS>
-__global__ __launch_bounds__(kThreads) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
                                                   const E* __restrict__ V,
                                                   const float* __restrict__ rowmax,
                                                   const uint8_t* __restrict__ blkc, Params P,
                                                   float* __restrict__ tau_out,
                                                   uint8_t* __restrict__ mask_out,
                                                   uint8_t* __restrict__ iters_out,
-                                                  void* __restrict__ out) {
+                                                  void* __restrict__ out, int* __restrict__ queue) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KS = row_stride<E, D>();
   constexpr bool kFusePV = sizeof(E) == 2;   // bf16: P V runs here, after tau
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, h = lane >> 5, c32 = lane & 31;
   const int N = P.N;
-  int bh, qtile;
-  map_tile((N + kBQW - 1) / kBQW, P.BH, P.causal, bh, qtile);
-  const int q0 = qtile * kBQW;
-  const int wq0 = q0 + kBQ * w;
-  const int iq = wq0 + c32;
-  const bool valid = iq < N;
-  const bool wave_rows = wq0 < N;
-  const int r32 = qtile * kWaves + w;
-  const E* Qh = Q + (size_t)bh * P.ld * D;
-  const E* Kh = K + (size_t)bh * P.ld * D;
-  const bool dense = (P.flags & EA_FLAG_FORCE_DENSE) != 0;
+  // one work unit: query tile qtile of head bh
+  auto unit = [&](const int bh, const int qtile) {
+    // The thread index passes through an empty asm statement, so that nothing
+    // derived from it is hoisted out of the unit loop and kept live across it
+    // (which would cost the registers of two waves per SIMD).
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c32 = lane & 31;
+    const int q0 = qtile * kBQW;
+    const int wq0 = q0 + kBQ * w;
+    const int iq = wq0 + c32;
+    const bool valid = iq < N;
+    const bool wave_rows = wq0 < N;
+    const int r32 = qtile * kWaves + w;
+    const E* Qh = Q + (size_t)bh * P.ld * D;
+    const E* Kh = K + (size_t)bh * P.ld * D;
+    const bool dense = (P.flags & EA_FLAG_FORCE_DENSE) != 0;
 
-  // histogram rows are padded by one bin so the 32 rows of a wave updating
-  // the same bin index do not hit the same LDS bank
-  constexpr int HROW = BINS * 2 + 2;
-  const int n_words = (P.n_kt + 31) >> 5;
-  char* kbuf = smem;                                                  // 2 x [64][KS]
-  unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem + 2 * kBK * KS);
-  short* list = reinterpret_cast<short*>(smem + 2 * kBK * KS + tau_region_bytes<E, D>(BINS));
-  uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
-  uint8_t* flags = wbits + kChunk;
-  uint32_t* cbits = reinterpret_cast<uint32_t*>(flags + kChunk);      // [4][n_words]
-  int* counter = reinterpret_cast<int*>(cbits + kWaves * n_words);
-  uint32_t* mbits = reinterpret_cast<uint32_t*>(counter + 16);        // [4][n_words] final mask
-  uint32_t* lbits = mbits + kWaves * n_words;                         // [4][n_words] tiles above lo
-  uint32_t* hbits = lbits + kWaves * n_words;                         // [2][4][n_words] live halves
+    // histogram rows are padded by one bin so the 32 rows of a wave updating
+    // the same bin index do not hit the same LDS bank
+    constexpr int HROW = BINS * 2 + 2;
+    const int n_words = (P.n_kt + 31) >> 5;
+    char* kbuf = smem;                                                  // 2 x [64][KS]
+    unsigned long long* hist = reinterpret_cast<unsigned long long*>(smem + 2 * kBK * KS);
+    short* list = reinterpret_cast<short*>(smem + 2 * kBK * KS + tau_region_bytes<E, D>(BINS));
+    uint8_t* wbits = reinterpret_cast<uint8_t*>(list + kChunk);
+    uint8_t* flags = wbits + kChunk;
+    uint32_t* cbits = reinterpret_cast<uint32_t*>(flags + kChunk);      // [4][n_words]
+    int* counter = reinterpret_cast<int*>(cbits + kWaves * n_words);
+    uint32_t* mbits = reinterpret_cast<uint32_t*>(counter + 16);        // [4][n_words] final mask
+    uint32_t* lbits = mbits + kWaves * n_words;                         // [4][n_words] tiles above lo
+    uint32_t* hbits = lbits + kWaves * n_words;                         // [2][4][n_words] live halves
 
-  const int wq_last = min(N - 1, wq0 + kBQ - 1);
-  const int kt_end_w = !wave_rows ? 0 : (P.causal ? wq_last / kBK + 1 : P.n_kt);
-  const int kt_end = P.causal ? (min(N - 1, q0 + kBQW - 1) / kBK + 1) : P.n_kt;
-  const bool wave_has_tail = wq0 + kBQ > N;
-  // this wave's block codes; one 16-byte chunk per lane covers 1024 tiles
-  const uint8_t* crow = blkc + ((size_t)bh * P.n_q32 + (size_t)min(r32, P.n_q32 - 1)) * blk_row(P.n_kt);
-  u32x4 pre = u32x4{~0u, ~0u, ~0u, ~0u};
-  if (16 * lane < kt_end_w) pre = *reinterpret_cast<const u32x4*>(crow + 16 * lane);
+    const int wq_last = min(N - 1, wq0 + kBQ - 1);
+    const int kt_end_w = !wave_rows ? 0 : (P.causal ? wq_last / kBK + 1 : P.n_kt);
+    const int kt_end = P.causal ? (min(N - 1, q0 + kBQW - 1) / kBK + 1) : P.n_kt;
+    const bool wave_has_tail = wq0 + kBQ > N;
+    // this wave's block codes; one 16-byte chunk per lane covers 1024 tiles
+    const uint8_t* crow = blkc + ((size_t)bh * P.n_q32 + (size_t)min(r32, P.n_q32 - 1)) * blk_row(P.n_kt);
+    u32x4 pre = u32x4{~0u, ~0u, ~0u, ~0u};
+    if (16 * lane < kt_end_w) pre = *reinterpret_cast<const u32x4*>(crow + 16 * lane);
 
-  Frag<E> qf[D / 16];
-  load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
+    Frag<E> qf[D / 16];
+    load_qfrags<E, D>(qf, Qh + (size_t)iq * D, valid, h);
 
-  // ---- provable bracket [lo, hi]:  f(max x - 1) >= 0 >= f(max x - n^(1-alpha))
-  const float xmax = valid ? rowmax[(size_t)bh * N + iq] : 0.0f;
-  float lo = 0.0f, hi = 0.0f, tau = 0.0f;
-  if (valid) {
-    const double dl = (double)xmax - 1.0;
-    lo = (float)dl;
-    if ((double)lo > dl) lo = nextafterf(lo, -INFINITY);
-    const double n = P.causal ? (double)(iq + 1) : (double)N;
-    const double dh = (double)xmax - pow(n, 1.0 - (double)P.alpha);
-    hi = (float)dh;
-    if ((double)hi < dh) hi = nextafterf(hi, INFINITY);
-    if (hi < lo) hi = lo;
-  }
-  bool conv = !valid;
-  int iters = 0;
-
-  // ---- candidate key tiles: bit kt of wave w is set when the block code of
-  // tile kt admits a score above some row's lower bracket end (tau >= lo, so
-  // no other tile can hold a nonzero probability for the wave).  The test
-  // compares the code with the smallest lo_i - max_j x_ij of the wave's rows,
-  // less a margin for the float rounding of both sides.  Words past the
-  // wave's last visible tile are written as zeros up to the workgroup's end.
-  // The first call (use_pre) also leaves each wave's strong tiles in mbits
-  // for the two-pass histogram (below): its candidates with block code 0,
-  // which hold the highest scores of some of its rows.  It returns the
-  // number of the workgroup's lanes that hold other candidates.
-  constexpr bool kStrongAK = AK == AK15 || AK == AK20;
-  const bool strong_pass = kStrongAK && !dense && P.mode == EA_TAU_HIST_HALLEY;
-  auto make_cand = [&](auto use_pre) -> int {
-    __syncthreads();   // earlier readers of the bits are done
-    // (the MFMA shapes of the row-max sweep and of this kernel round their
-    // partial sums differently: 64 float epsilons of |x| covers that)
-    float th = valid ? (lo - xmax) - 64.0f * FLT_EPSILON * (fmaxf(1.0f, fabsf(xmax)) + 2.0f) : INFINITY;
-    th = half_min32(th);           // both lane halves hold the same 32 rows
-    const float lim = -128.0f * th;   // candidate iff code < lim
-    int weak = 0;
-    for (int base = 0; base < kt_end; base += 64 * 16) {
-      const int t0 = base + 16 * lane;
-      u32x4 r = u32x4{~0u, ~0u, ~0u, ~0u};
-      if (decltype(use_pre)::value && base == 0)
-        r = pre;
-      else if (t0 < kt_end_w)
-        r = *reinterpret_cast<const u32x4*>(crow + t0);
-      uint32_t bits = 0, sb = 0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t c = (r[j >> 2] >> (8 * (j & 3))) & 0xFFu;
-        if ((float)c < lim && t0 + j < kt_end_w) {
-          bits |= 1u << j;
-          if (c == 0u) sb |= 1u << j;
-        }
-      }
-      const int nv = min(max(kt_end_w - t0, 0), 16);
-      if (dense) bits = nv >= 16 ? 0xFFFFu : ((1u << nv) - 1u);
-      // lanes 2m and 2m+1 hold the two halves of word (base / 32) + m
-      const uint32_t word = bits | (dpp_u<0xB1>(bits) << 16);
-      const int wd = (base >> 5) + (lane >> 1);
-      if (!(lane & 1) && wd < n_words) cbits[w * n_words + wd] = word;
-      if constexpr (decltype(use_pre)::value) {
-        if (strong_pass) {
-          weak |= (bits & ~sb) != 0u;
-          const uint32_t sword = sb | (dpp_u<0xB1>(sb) << 16);
-          if (!(lane & 1) && wd < n_words) mbits[w * n_words + wd] = sword;
-        }
-      }
-    }
-    // (lanes that hold other candidates, per wave, beside build_list's counter)
-    if (decltype(use_pre)::value && strong_pass) {
-      const int nw = __popcll(__ballot(weak));
-      if (lane == 0) counter[4 + w] = nw;
-    }
-    __syncthreads();
-    if (decltype(use_pre)::value && strong_pass) return counter[4] + counter[5] + counter[6] + counter[7];
-    return 0;
-  };
-  auto cand = [&](int ww, int kt) -> bool { return (cbits[ww * n_words + (kt >> 5)] >> (kt & 31)) & 1u; };
-  const int weak_lanes = make_cand(std::true_type{});
-
-  // ---- histogram initialisation (AdaSplash-2)
-  if (P.mode == EA_TAU_HIST_HALLEY) {
-    for (int e = threadIdx.x; e < kBQW * HROW; e += kThreads) hist[e] = 0ull;
-    unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * HROW;
-    // Bins split [lo, hi]; moments are kept in units of 1/(2^S - 1) of y = x - lo <= 1
-    // with Y <= 2^S - 1: the count sits at bit 40, sum Y below it and sum Y^2
-    // in a word of its own, so with at most N <= 2^(40-S) elements per bin
-    // sum Y < 2^40 and sum Y^2 < 2^64.  S = 24 up to N = 65536, fewer bits
-    // beyond (the host chooses S from N).
-    const float width = valid ? fmaxf(hi - lo, 1e-30f) : 1.0f;
-    const float bin_scale = (float)BINS / width;
-    const float ysc = (float)((1u << P.hshift) - 1u);
-    const uint32_t hrow = (uint32_t)reinterpret_cast<uintptr_t>(hr);
-    const float lo0 = lo;   // the histogram's origin
-    // Histogram passes: 0 takes every candidate tile.  For alpha in {1.5, 2}
-    // there are two instead: pass 1 takes the strong tiles only (each wave's
-    // candidates with block code 0, joined over the workgroup).  f of their
-    // scores alone
-    // lies below f, so their histogram's highest edge with f >= 0 is a lower
-    // bound on tau; it prunes the candidates, and pass 2 adds the remaining
-    // candidates of the raised bound.  Every score above that bound is then
-    // in the histogram, so f at every edge above it, tau's bin, the start and
-    // the narrowed bracket come out as from pass 0; only tiles that cannot
-    // reach the bound are skipped.
-    auto strong = [&](int kt) -> bool { return (lbits[kt >> 5] >> (kt & 31)) & 1u; };
-    // two passes only when the workgroup holds enough other candidates to
-    // skip some of them
-    const bool two = strong_pass && weak_lanes > kStrongMinWeak;
-    if (two) {
-      // the union of the waves' strong tiles, in lbits (first written by the sweeps)
-      for (int e = threadIdx.x; e < n_words; e += kThreads)
-        lbits[e] = mbits[e] | mbits[n_words + e] | mbits[2 * n_words + e] | mbits[3 * n_words + e];
-      __syncthreads();
-    }
-    const int hp_first = two ? 1 : 0, hp_last = two ? 2 : 0;
-#pragma clang loop unroll(disable)
-    for (int hp = hp_first; hp <= hp_last; ++hp) {
-      if (hp == 2) {
-        wait_lds();
-        if (valid) {
-          const int b = hist_floor_bin<AK, BINS>(hr, width, P.hshift);
-          if (b > 0) lo = fmaxf(lo, hist_edge(lo0, (double)b * ((double)width / BINS), xmax, P.hshift, -1.0f));
-        }
-        make_cand(std::false_type{});
-      }
-      auto pred = [&](int ww, int kt) -> bool {
-        return cand(ww, kt) && (hp == 0 || (hp == 1) == strong(kt));
-      };
-      for (int base = 0; base < kt_end; base += kChunk) {
-        const int n = build_list(base, min(kChunk, kt_end - base), pred, list, wbits, flags, counter);
-        RowTiles<E, D, kBK> st(Kh, N, w, lane);
-        if (n > 0) {
-          st.fetch(kbuf, (base + list[0]) * kBK);
-          st.commit(kbuf);
-        }
-        __syncthreads();
-        for (int i = 0; i < n; ++i) {
-          const int kt = base + list[i];
-          if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
-          if ((wbits[i] >> w) & 1) {
-            auto body = [&](auto masked) {
-              f32x16 acc[2];
-              tile_scores<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane,
-                                row_limit(kt * kBK, iq, N, P.causal, h), masked);
-#pragma unroll
-              for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                  hist_add<true>(hrow, hr, clamp01(fmaf(acc[kb][j], P.scale, -lo0)), bin_scale, ysc, BINS);
-                }
-            };
-            if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
-              body(std::true_type{});
-            else
-              body(std::false_type{});
-          }
-          if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
-          __syncthreads();
-        }
-      }
-    }
-    wait_lds();
+    // ---- provable bracket [lo, hi]:  f(max x - 1) >= 0 >= f(max x - n^(1-alpha))
+    const float xmax = valid ? rowmax[(size_t)bh * N + iq] : 0.0f;
+    float lo = 0.0f, hi = 0.0f, tau = 0.0f;
     if (valid) {
-      float lo_h = lo0;
-      hist_start<AK, BINS>(hr, width, xmax, P.hshift, P.beta, lo_h, hi, tau);
-      lo = fmaxf(lo, lo_h);
-      tau = fminf(fmaxf(tau, lo), hi);
+      const double dl = (double)xmax - 1.0;
+      lo = (float)dl;
+      if ((double)lo > dl) lo = nextafterf(lo, -INFINITY);
+      // n^(1 - alpha) from the hardware log2 and exp2 (relative error a few
+      // 1e-6 for n <= 2^20), made 2^-16 smaller: hi only has to bound tau
+      // from above, and no double-precision pow stays live in the unit loop
+      const float n = P.causal ? (float)(iq + 1) : (float)N;
+      const float g = __builtin_amdgcn_exp2f((1.0f - P.alpha) * __builtin_amdgcn_logf(n)) * (1.0f - 0x1p-16f);
+      const double dh = (double)xmax - (double)g;
+      hi = (float)dh;
+      if ((double)hi < dh) hi = nextafterf(hi, INFINITY);
+      if (hi < lo) hi = lo;
     }
-    // the histogram narrowed lo to tau's bin: prune the candidates again
-    if (AK == AK15 || AK == AK20) make_cand(std::false_type{});
-  } else if (P.mode == EA_TAU_HALLEY_BISECT) {
-    tau = lo;
-  } else {
-    tau = 0.5f * (lo + hi);
-  }
+    bool conv = !valid;
+    int iters = 0;
 
-  // ---- refinement sweeps (Halley-bisection or bisection) over candidate tiles
-  // The final mask is kept as bits in LDS (the tile, and each 32-key half)
-  // and written to block_mask after the sweeps; the P V epilogue reads it too.
-  uint8_t* mrow = mask_out + (size_t)bh * P.mhs + (size_t)r32 * P.mrs;
-  for (int e = lane; e < n_words; e += kWave) {
-    const int nv = min(max(kt_end_w - 32 * e, 0), 32);
-    const uint32_t vis = dense ? (nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u)) : 0u;
-    mbits[w * n_words + e] = vis;
-    hbits[w * n_words + e] = vis;
-    hbits[(kWaves + w) * n_words + e] = vis;
-  }
-  const int max_iters = P.max_iters;
-  // The candidate tiles only shrink between refinement sweeps.  When the
-  // workgroup's fit beside the K double buffer in the histogram's space (dead
-  // from here), they are copied once and every sweep reads them in place: no
-  // list rebuild, copy or barrier per tile.
-  constexpr int kResident = 2 + tau_region_bytes<E, D>(BINS) / (kBK * KS);
-  // streaming sweeps: a ring over the same slots where tiles arrive by the
-  // LDS copy engine (bf16, d = 128); register-staged tiles keep two buffers
-  constexpr bool kDMA = sizeof(E) == 2 && D == 128;
-  constexpr int kRing = kDMA ? (kResident < 4 ? kResident : 4) : 2;
-  constexpr int kTileRowsPerWave = kBK / kWaves;   // copy instructions per wave and tile
-  auto slot = [&](int i) -> char* {
-    return i < 2 ? kbuf + i * kBK * KS : reinterpret_cast<char*>(hist) + (i - 2) * kBK * KS;
-  };
-  int n_res = -1;   // resident tile count, or -1: the sweeps stream their tiles
-  if (kt_end <= kChunk) {
-    const int n = build_list(0, kt_end, cand, list, wbits, flags, counter);
-    if (n <= kResident) {
-      RowTiles<E, D, kBK> st(Kh, N, w, lane);
-      for (int i = 0; i < n; ++i) {
-        st.fetch(slot(i), list[i] * kBK);
-        st.commit(slot(i));
+    // ---- candidate key tiles: bit kt of wave w is set when the block code of
+    // tile kt admits a score above some row's lower bracket end (tau >= lo, so
+    // no other tile can hold a nonzero probability for the wave).  The test
+    // compares the code with the smallest lo_i - max_j x_ij of the wave's rows,
+    // less a margin for the float rounding of both sides.  Words past the
+    // wave's last visible tile are written as zeros up to the workgroup's end.
+    // The first call (use_pre) also leaves each wave's strong tiles in mbits
+    // for the two-pass histogram (below): its candidates with block code 0,
+    // which hold the highest scores of some of its rows.  It returns the
+    // number of the workgroup's lanes that hold other candidates.
+    constexpr bool kStrongAK = AK == AK15 || AK == AK20;
+    const bool strong_pass = kStrongAK && !dense && P.mode == EA_TAU_HIST_HALLEY;
+    auto make_cand = [&](auto use_pre) -> int {
+      __syncthreads();   // earlier readers of the bits are done
+      // (the MFMA shapes of the row-max sweep and of this kernel round their
+      // partial sums differently: 64 float epsilons of |x| covers that)
+      float th = valid ? (lo - xmax) - 64.0f * FLT_EPSILON * (fmaxf(1.0f, fabsf(xmax)) + 2.0f) : INFINITY;
+      th = half_min32(th);           // both lane halves hold the same 32 rows
+      const float lim = -128.0f * th;   // candidate iff code < lim
+      int weak = 0;
+      for (int base = 0; base < kt_end; base += 64 * 16) {
+        const int t0 = base + 16 * lane;
+        u32x4 r = u32x4{~0u, ~0u, ~0u, ~0u};
+        if (decltype(use_pre)::value && base == 0)
+          r = pre;
+        else if (t0 < kt_end_w)
+          r = *reinterpret_cast<const u32x4*>(crow + t0);
+        // (bits shifted in from the top: no mask constants to keep in registers)
+        uint32_t bits = 0, sb = 0;
+#pragma unroll
+        for (int j = 15; j >= 0; --j) {
+          const uint32_t c = (r[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+          const bool cj = (float)c < lim && t0 + j < kt_end_w;
+          bits = (bits << 1) | (uint32_t)cj;
+          sb = (sb << 1) | (uint32_t)(cj && c == 0u);
+        }
+        const int nv = min(max(kt_end_w - t0, 0), 16);
+        if (dense) bits = nv >= 16 ? 0xFFFFu : ((1u << nv) - 1u);
+        // lanes 2m and 2m+1 hold the two halves of word (base / 32) + m
+        const uint32_t word = bits | (dpp_u<0xB1>(bits) << 16);
+        const int wd = (base >> 5) + (lane >> 1);
+        if (!(lane & 1) && wd < n_words) cbits[w * n_words + wd] = word;
+        if constexpr (decltype(use_pre)::value) {
+          if (strong_pass) {
+            weak |= (bits & ~sb) != 0u;
+            const uint32_t sword = sb | (dpp_u<0xB1>(sb) << 16);
+            if (!(lane & 1) && wd < n_words) mbits[w * n_words + wd] = sword;
+          }
+        }
+      }
+      // (lanes that hold other candidates, per wave, beside build_list's counter)
+      if (decltype(use_pre)::value && strong_pass) {
+        const int nw = __popcll(__ballot(weak));
+        if (lane == 0) counter[4 + w] = nw;
       }
       __syncthreads();
-      n_res = n;
-    }
-  }
-  for (int sweep = 0; sweep <= max_iters + 1; ++sweep) {
-    const bool wave_busy = __ballot(!conv) != 0ull;
-    if (!__syncthreads_or(wave_busy ? 1 : 0)) break;
-    if (wave_busy && !dense) {
-      // this sweep rewrites the wave's mask and its tiles above lo
-      for (int e = lane; e < n_words; e += kWave) {
-        mbits[w * n_words + e] = 0u;
-        hbits[w * n_words + e] = 0u;
-        hbits[(kWaves + w) * n_words + e] = 0u;
-        lbits[w * n_words + e] = 0u;
-      }
-    }
-    float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
-    // This wave's bits of the 32-tile word it is walking (final mask and tiles
-    // above lo), kept in wave-uniform registers and written to LDS when the
-    // walk leaves the word: an LDS write inside the tile loop would make the
-    // wave wait for the next tile's copy in flight (the compiler cannot tell
-    // the two LDS destinations apart), which would expose the copy's latency.
-    // Tiles are listed in increasing order and a word never spans two list
-    // chunks, so every word is written at most once per sweep.
-    int bit_wd = -1;
-    uint32_t m_word = 0u, l_word = 0u, h0_word = 0u, h1_word = 0u;
-    auto flush_bits = [&]() {
-      if (bit_wd >= 0 && lane == 0) {
-        mbits[w * n_words + bit_wd] = m_word;
-        hbits[w * n_words + bit_wd] = h0_word;
-        hbits[(kWaves + w) * n_words + bit_wd] = h1_word;
-        lbits[w * n_words + bit_wd] = l_word;
-      }
-      bit_wd = -1;
-      m_word = l_word = h0_word = h1_word = 0u;
+      if (decltype(use_pre)::value && strong_pass) return counter[4] + counter[5] + counter[6] + counter[7];
+      return 0;
     };
-    // f, f', f'' terms of key tile kt (staged at kl) and its mask bits
-    auto sweep_tile = [&](int kt, const char* kl) {
-      auto body = [&](auto masked) {
-        const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
-        f32x16 acc[2];
-        float cnt_at[3];
-        cnt_at[0] = Ent<AK>::count(F0, F1, F2, cnt);
-        tile_scores<E, D>(acc, kl, KS, qf, lane, lim, masked);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
-            Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
+    auto cand = [&](int ww, int kt) -> bool { return (cbits[ww * n_words + (kt >> 5)] >> (kt & 31)) & 1u; };
+    const int weak_lanes = make_cand(std::true_type{});
+
+    // ---- histogram initialisation (AdaSplash-2)
+    if (P.mode == EA_TAU_HIST_HALLEY) {
+      for (int e = threadIdx.x; e < kBQW * HROW; e += kThreads) hist[e] = 0ull;
+      unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * HROW;
+      // Bins split [lo, hi]; moments are kept in units of 1/(2^S - 1) of y = x - lo <= 1
+      // with Y <= 2^S - 1: the count sits at bit 40, sum Y below it and sum Y^2
+      // in a word of its own, so with at most N <= 2^(40-S) elements per bin
+      // sum Y < 2^40 and sum Y^2 < 2^64.  S = 24 up to N = 65536, fewer bits
+      // beyond (the host chooses S from N).
+      const float width = valid ? fmaxf(hi - lo, 1e-30f) : 1.0f;
+      const float bin_scale = (float)BINS / width;
+      const float ysc = (float)((1u << P.hshift) - 1u);
+      const uint32_t hrow = (uint32_t)reinterpret_cast<uintptr_t>(hr);
+      const float lo0 = lo;   // the histogram's origin
+      // Histogram passes: 0 takes every candidate tile.  For alpha in {1.5, 2}
+      // there are two instead: pass 1 takes the strong tiles only (each wave's
+      // candidates with block code 0, joined over the workgroup).  f of their
+      // scores alone
+      // lies below f, so their histogram's highest edge with f >= 0 is a lower
+      // bound on tau; it prunes the candidates, and pass 2 adds the remaining
+      // candidates of the raised bound.  Every score above that bound is then
+      // in the histogram, so f at every edge above it, tau's bin, the start and
+      // the narrowed bracket come out as from pass 0; only tiles that cannot
+      // reach the bound are skipped.
+      auto strong = [&](int kt) -> bool { return (lbits[kt >> 5] >> (kt & 31)) & 1u; };
+      // two passes only when the workgroup holds enough other candidates to
+      // skip some of them
+      const bool two = strong_pass && weak_lanes > kStrongMinWeak;
+      if (two) {
+        // the union of the waves' strong tiles, in lbits (first written by the sweeps)
+        for (int e = threadIdx.x; e < n_words; e += kThreads)
+          lbits[e] = mbits[e] | mbits[n_words + e] | mbits[2 * n_words + e] | mbits[3 * n_words + e];
+        __syncthreads();
+      }
+      const int hp_first = two ? 1 : 0, hp_last = two ? 2 : 0;
+#pragma clang loop unroll(disable)
+      for (int hp = hp_first; hp <= hp_last; ++hp) {
+        if (hp == 2) {
+          wait_lds();
+          if (valid) {
+            const int b = hist_floor_bin<AK, BINS>(hr, width, P.hshift);
+            if (b > 0) lo = fmaxf(lo, hist_edge(lo0, (double)b * ((double)width / BINS), xmax, P.hshift, -1.0f));
           }
-          cnt_at[kb + 1] = Ent<AK>::count(F0, F1, F2, cnt);
+          make_cand(std::false_type{});
+          for (int e = lane; e < n_words; e += kWave) mbits[w * n_words + e] = 0u;
         }
-        if (!dense) {
-          const bool any0 = __ballot(cnt_at[1] > cnt_at[0]) != 0ull;
-          const bool any1 = __ballot(cnt_at[2] > cnt_at[1]) != 0ull;
-          const bool any = any0 || any1;
-          // does the tile hold a score above some row's lower bracket end?
-          float mx = fmax_nan(acc[0][0], acc[1][0]);
-#pragma unroll
-          for (int j = 1; j < 16; ++j) mx = fmax_nan(mx, fmax_nan(acc[0][j], acc[1][j]));
-          // (the ballot runs on every lane: it must see every row)
-          const bool above = __ballot(fmaf(mx, P.scale, -lo) > 0.0f) != 0ull;
-          const int wd = __builtin_amdgcn_readfirstlane(kt >> 5);
-          if (wd != bit_wd) {
-            flush_bits();
-            bit_wd = wd;
-          }
-          if (any) m_word |= 1u << (kt & 31);
-          if (any0) h0_word |= 1u << (kt & 31);
-          if (any1) h1_word |= 1u << (kt & 31);
-          if (above) l_word |= 1u << (kt & 31);
-        }
-      };
-      if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
-        body(std::true_type{});
-      else
-        body(std::false_type{});
-    };
-    if (n_res >= 0) {
-      for (int i = 0; i < n_res; ++i)
-        if (wave_busy && cand(w, list[i])) sweep_tile(list[i], slot(i));
-      flush_bits();
-    } else {
-      for (int base = 0; base < kt_end; base += kChunk) {
-        const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
-        RowTiles<E, D, kBK> st(Kh, N, w, lane);
-        if constexpr (kRing > 2) {
-          // Copy ring of kRing tile slots (the histogram's space holds two of
-          // them): tile i sits in slot i % kRing and up to kRing - 1 copies are
-          // in flight, so a copy has several tiles' work to land.  Nothing else
-          // touches vector memory in this loop, so the wave's outstanding
-          // copies are counted exactly.
-#pragma unroll
-          for (int j = 0; j < kRing - 1; ++j)
-            if (j < n) st.fetch(slot(j), (base + list[j]) * kBK);
-          for (int i = 0; i < n; ++i) {
-            // tile i has landed once at most the copies of tiles i+1 .. are in flight
-            const int ahead = min(kRing - 2, n - 1 - i);
-            if (ahead >= 2) wait_vmcnt<2 * kTileRowsPerWave>();
-            else if (ahead == 1) wait_vmcnt<kTileRowsPerWave>();
-            else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();   // every wave's part of tile i; slot of tile i-1 free
-            if (i + kRing - 1 < n) st.fetch(slot((i + kRing - 1) % kRing), (base + list[i + kRing - 1]) * kBK);
-            if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(base + list[i], slot(i % kRing));
-          }
-          __syncthreads();
-        } else {
+        // Pass 2 also marks, per wave, the tiles where some row has a score
+        // above its own raised bound (less a rounding margin), kept in mbits.
+        // The block codes test a 32-row block against its loosest row; these
+        // bits test every row against its own bound, and tau's bin only lies
+        // higher, so they prune the first refinement sweep's candidates.
+        const float gy = valid ? (lo - lo0) - 4.0f * FLT_EPSILON * (fmaxf(1.0f, fabsf(xmax)) + 2.0f) : 2.0f;
+        int bit_wd = -1;
+        uint32_t r_word = 0u;
+        auto flush_row_bits = [&]() {
+          if (bit_wd >= 0 && lane == 0) mbits[w * n_words + bit_wd] = r_word;
+          bit_wd = -1;
+          r_word = 0u;
+        };
+        auto pred = [&](int ww, int kt) -> bool {
+          return cand(ww, kt) && (hp == 0 || (hp == 1) == strong(kt));
+        };
+        for (int base = 0; base < kt_end; base += kChunk) {
+          const int n = build_list(base, min(kChunk, kt_end - base), pred, list, wbits, flags, counter);
+          RowTiles<E, D, kBK> st(Kh, N, w, lane);
           if (n > 0) {
             st.fetch(kbuf, (base + list[0]) * kBK);
             st.commit(kbuf);
           }
           __syncthreads();
           for (int i = 0; i < n; ++i) {
+            const int kt = base + list[i];
             if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
-            if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(base + list[i], kbuf + (i & 1) * kBK * KS);
+            if ((wbits[i] >> w) & 1) {
+              float ymax = 0.0f;
+              auto body = [&](auto masked) {
+                f32x16 acc[2];
+                tile_scores<E, D>(acc, kbuf + (i & 1) * kBK * KS, KS, qf, lane,
+                                  row_limit(kt * kBK, iq, N, P.causal, h), masked);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                  for (int j = 0; j < 16; ++j) {
+                    const float yc = clamp01(fmaf(acc[kb][j], P.scale, -lo0));
+                    ymax = fmaxf(ymax, yc);
+                    hist_add<true>(hrow, hr, yc, bin_scale, ysc, BINS);
+                  }
+              };
+              if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+                body(std::true_type{});
+              else
+                body(std::false_type{});
+              if (hp == 2) {
+                // (the ballot runs on every lane: it must see every row)
+                const bool above = __ballot(ymax > gy) != 0ull;
+                const int wd = __builtin_amdgcn_readfirstlane(kt >> 5);
+                if (wd != bit_wd) {
+                  flush_row_bits();
+                  bit_wd = wd;
+                }
+                if (above) r_word |= 1u << (kt & 31);
+              }
+            }
             if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
             __syncthreads();
           }
+          flush_row_bits();
         }
-        flush_bits();
       }
-    }
-    F0 += __shfl_xor(F0, 32);
-    F1 += __shfl_xor(F1, 32);
-    F2 += __shfl_xor(F2, 32);
-    tau_step<AK>(F0, F1, F2, P.beta, P.mode, P.tol, max_iters, lo, hi, tau, conv, iters);
-    // Candidates of the next sweep: tau only moves up from lo, so a tile with
-    // no score above the lo this sweep used stays empty for every row; a wave
-    // whose rows have all converged needs none.  (Only this wave's bits are
-    // written; every reader of them passed a barrier since its last read.)
-    if (wave_busy && !dense) {
-      const bool busy_next = __ballot(!conv) != 0ull;
-      for (int e = lane; e < n_words; e += kWave) cbits[w * n_words + e] = busy_next ? lbits[w * n_words + e] : 0u;
-    }
-  }
-
-  // block_mask row of this wave from the final bits (every tile, so no zero fill)
-  if (wave_rows) {
-    for (int kt = lane; kt < P.n_kt; kt += kWave) {
-      const uint32_t b = 1u << (kt & 31), e = (uint32_t)(kt >> 5);
-      const bool m = mbits[w * n_words + e] & b;
-      const uint32_t v = m ? (1u | ((hbits[w * n_words + e] & b) ? 2u : 0u) |
-                              ((hbits[(kWaves + w) * n_words + e] & b) ? 4u : 0u))
-                           : 0u;
-      mrow[kt] = (uint8_t)v;
-    }
-  }
-  if (valid && h == 0) {
-    tau_out[(size_t)bh * P.ld + iq] = tau;
-    if (iters_out) iters_out[(size_t)bh * P.ld + iq] = (uint8_t)min(iters, 255);
-  }
-
-  // ---- P V over the active tiles of the final mask (bf16).  Q is still in
-  // registers, tau in a register and the mask in LDS; V tiles take the
-  // histogram's place.
-  if constexpr (kFusePV) {
-    __syncthreads();   // every wave's final mask bits (and the histogram is dead)
-    char* vbuf = reinterpret_cast<char*>(hist);                       // 2 x [64][KS]
-    const E* Vh = V + (size_t)bh * P.ld * D;
-    const float ptau = valid ? tau : INFINITY;
-    f32x16 oacc[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-    auto active = [&](int ww, int kt) -> bool { return (mbits[ww * n_words + (kt >> 5)] >> (kt & 31)) & 1u; };
-    RowTiles<E, D, kBK> sk(Kh, N, w, lane), sv(Vh, N, w, lane);
-    for (int base = 0; base < kt_end; base += kChunk) {
-      const int n = build_list(base, min(kChunk, kt_end - base), active, list, wbits, flags, counter);
-      if (n > 0) {
-        sk.fetch(kbuf, (base + list[0]) * kBK);
-        sv.fetch(vbuf, (base + list[0]) * kBK);
-        sk.commit(kbuf);
-        sv.commit(vbuf);
+      wait_lds();
+      if (valid) {
+        float lo_h = lo0;
+        hist_start<AK, BINS>(hr, width, xmax, P.hshift, P.beta, lo_h, hi, tau);
+        lo = fmaxf(lo, lo_h);
+        tau = fminf(fmaxf(tau, lo), hi);
       }
-      __syncthreads();
-      for (int i = 0; i < n; ++i) {
-        const int kt = base + list[i];
-        const int nb = (i + 1) & 1;
-        if (i + 1 < n) {
-          sk.fetch(kbuf + nb * kBK * KS, (base + list[i + 1]) * kBK);
-          sv.fetch(vbuf + nb * kBK * KS, (base + list[i + 1]) * kBK);
-        }
-        if ((wbits[i] >> w) & 1) {
-          const char* kl = kbuf + (i & 1) * kBK * KS;
-          const char* vl = vbuf + (i & 1) * kBK * KS;
-          const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
-          if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
-            pv_tile<E, D, AK, true>(oacc, kl, vl, KS, qf, lane, lim, ptau, P);
-          else
-            pv_tile<E, D, AK, false>(oacc, kl, vl, KS, qf, lane, lim, ptau, P);
-        }
-        if (i + 1 < n) {
-          sk.commit(kbuf + nb * kBK * KS);
-          sv.commit(vbuf + nb * kBK * KS);
-        }
+      // the histogram narrowed lo to tau's bin: prune the candidates again
+      if (AK == AK15 || AK == AK20) make_cand(std::false_type{});
+      if (two) {
+        // only tiles where some row passed its own raised bound, or strong ones
+        for (int e = lane; e < n_words; e += kWave)
+          cbits[w * n_words + e] &= mbits[w * n_words + e] | lbits[e];
         __syncthreads();
       }
+    } else if (P.mode == EA_TAU_HALLEY_BISECT) {
+      tau = lo;
+    } else {
+      tau = 0.5f * (lo + hi);
     }
-    if (valid) store_out<D>(oacc, out, (size_t)bh * P.ld + iq, h, P.out_bf16 != 0);
+
+    // ---- refinement sweeps (Halley-bisection or bisection) over candidate tiles
+    // The final mask is kept as bits in LDS (the tile, and each 32-key half)
+    // and written to block_mask after the sweeps; the P V epilogue reads it too.
+    uint8_t* mrow = mask_out + (size_t)bh * P.mhs + (size_t)r32 * P.mrs;
+    for (int e = lane; e < n_words; e += kWave) {
+      const int nv = min(max(kt_end_w - 32 * e, 0), 32);
+      const uint32_t vis = dense ? (nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u)) : 0u;
+      mbits[w * n_words + e] = vis;
+      hbits[w * n_words + e] = vis;
+      hbits[(kWaves + w) * n_words + e] = vis;
+    }
+    const int max_iters = P.max_iters;
+    // The candidate tiles only shrink between refinement sweeps.  When the
+    // workgroup's fit beside the K double buffer in the histogram's space (dead
+    // from here), they are copied once and every sweep reads them in place: no
+    // list rebuild, copy or barrier per tile.
+    constexpr int kResident = 2 + tau_region_bytes<E, D>(BINS) / (kBK * KS);
+    // streaming sweeps: a ring over the same slots where tiles arrive by the
+    // LDS copy engine (bf16, d = 128); register-staged tiles keep two buffers
+    constexpr bool kDMA = sizeof(E) == 2 && D == 128;
+    constexpr int kRing = kDMA ? (kResident < 4 ? kResident : 4) : 2;
+    constexpr int kTileRowsPerWave = kBK / kWaves;   // copy instructions per wave and tile
+    auto slot = [&](int i) -> char* {
+      return i < 2 ? kbuf + i * kBK * KS : reinterpret_cast<char*>(hist) + (i - 2) * kBK * KS;
+    };
+    int n_res = -1;   // resident tile count, or -1: the sweeps stream their tiles
+    if (kt_end <= kChunk) {
+      const int n = build_list(0, kt_end, cand, list, wbits, flags, counter);
+      if (n <= kResident) {
+        RowTiles<E, D, kBK> st(Kh, N, w, lane);
+        for (int i = 0; i < n; ++i) {
+          st.fetch(slot(i), list[i] * kBK);
+          st.commit(slot(i));
+        }
+        __syncthreads();
+        n_res = n;
+      }
+    }
+    for (int sweep = 0; sweep <= max_iters + 1; ++sweep) {
+      const bool wave_busy = __ballot(!conv) != 0ull;
+      if (!__syncthreads_or(wave_busy ? 1 : 0)) break;
+      if (wave_busy && !dense) {
+        // this sweep rewrites the wave's mask and its tiles above lo
+        for (int e = lane; e < n_words; e += kWave) {
+          mbits[w * n_words + e] = 0u;
+          hbits[w * n_words + e] = 0u;
+          hbits[(kWaves + w) * n_words + e] = 0u;
+          lbits[w * n_words + e] = 0u;
+        }
+      }
+      float F0 = 0, F1 = 0, F2 = 0, cnt = 0;
+      // This wave's bits of the 32-tile word it is walking (final mask and tiles
+      // above lo), kept in wave-uniform registers and written to LDS when the
+      // walk leaves the word: an LDS write inside the tile loop would make the
+      // wave wait for the next tile's copy in flight (the compiler cannot tell
+      // the two LDS destinations apart), which would expose the copy's latency.
+      // Tiles are listed in increasing order and a word never spans two list
+      // chunks, so every word is written at most once per sweep.
+      int bit_wd = -1;
+      uint32_t m_word = 0u, l_word = 0u, h0_word = 0u, h1_word = 0u;
+      auto flush_bits = [&]() {
+        if (bit_wd >= 0 && lane == 0) {
+          mbits[w * n_words + bit_wd] = m_word;
+          hbits[w * n_words + bit_wd] = h0_word;
+          hbits[(kWaves + w) * n_words + bit_wd] = h1_word;
+          lbits[w * n_words + bit_wd] = l_word;
+        }
+        bit_wd = -1;
+        m_word = l_word = h0_word = h1_word = 0u;
+      };
+      // f, f', f'' terms of key tile kt (staged at kl) and its mask bits
+      auto sweep_tile = [&](int kt, const char* kl) {
+        auto body = [&](auto masked) {
+          const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
+          f32x16 acc[2];
+          float cnt_at[3];
+          cnt_at[0] = Ent<AK>::count(F0, F1, F2, cnt);
+          tile_scores<E, D>(acc, kl, KS, qf, lane, lim, masked);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+              const float t = clamp01(fmaf(acc[kb][j], P.scale, -tau));
+              Ent<AK>::sweep(t, P.beta, F0, F1, F2, cnt);
+            }
+            cnt_at[kb + 1] = Ent<AK>::count(F0, F1, F2, cnt);
+          }
+          if (!dense) {
+            const bool any0 = __ballot(cnt_at[1] > cnt_at[0]) != 0ull;
+            const bool any1 = __ballot(cnt_at[2] > cnt_at[1]) != 0ull;
+            const bool any = any0 || any1;
+            // does the tile hold a score above some row's lower bracket end?
+            float mx = fmax_nan(acc[0][0], acc[1][0]);
+#pragma unroll
+            for (int j = 1; j < 16; ++j) mx = fmax_nan(mx, fmax_nan(acc[0][j], acc[1][j]));
+            // (the ballot runs on every lane: it must see every row)
+            const bool above = __ballot(fmaf(mx, P.scale, -lo) > 0.0f) != 0ull;
+            const int wd = __builtin_amdgcn_readfirstlane(kt >> 5);
+            if (wd != bit_wd) {
+              flush_bits();
+              bit_wd = wd;
+            }
+            if (any) m_word |= 1u << (kt & 31);
+            if (any0) h0_word |= 1u << (kt & 31);
+            if (any1) h1_word |= 1u << (kt & 31);
+            if (above) l_word |= 1u << (kt & 31);
+          }
+        };
+        if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+          body(std::true_type{});
+        else
+          body(std::false_type{});
+      };
+      if (n_res >= 0) {
+        for (int i = 0; i < n_res; ++i)
+          if (wave_busy && cand(w, list[i])) sweep_tile(list[i], slot(i));
+        flush_bits();
+      } else {
+        for (int base = 0; base < kt_end; base += kChunk) {
+          const int n = build_list(base, min(kChunk, kt_end - base), cand, list, wbits, flags, counter);
+          RowTiles<E, D, kBK> st(Kh, N, w, lane);
+          if constexpr (kRing > 2) {
+            // Copy ring of kRing tile slots (the histogram's space holds two of
+            // them): tile i sits in slot i % kRing and up to kRing - 1 copies are
+            // in flight, so a copy has several tiles' work to land.  Nothing else
+            // touches vector memory in this loop, so the wave's outstanding
+            // copies are counted exactly.
+#pragma unroll
+            for (int j = 0; j < kRing - 1; ++j)
+              if (j < n) st.fetch(slot(j), (base + list[j]) * kBK);
+            for (int i = 0; i < n; ++i) {
+              // tile i has landed once at most the copies of tiles i+1 .. are in flight
+              const int ahead = min(kRing - 2, n - 1 - i);
+              if (ahead >= 2) wait_vmcnt<2 * kTileRowsPerWave>();
+              else if (ahead == 1) wait_vmcnt<kTileRowsPerWave>();
+              else wait_vmcnt<0>();
+              __builtin_amdgcn_s_barrier();   // every wave's part of tile i; slot of tile i-1 free
+              if (i + kRing - 1 < n) st.fetch(slot((i + kRing - 1) % kRing), (base + list[i + kRing - 1]) * kBK);
+              if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(base + list[i], slot(i % kRing));
+            }
+            __syncthreads();
+          } else {
+            if (n > 0) {
+              st.fetch(kbuf, (base + list[0]) * kBK);
+              st.commit(kbuf);
+            }
+            __syncthreads();
+            for (int i = 0; i < n; ++i) {
+              if (i + 1 < n) st.fetch(kbuf + ((i + 1) & 1) * kBK * KS, (base + list[i + 1]) * kBK);
+              if (wave_busy && ((wbits[i] >> w) & 1)) sweep_tile(base + list[i], kbuf + (i & 1) * kBK * KS);
+              if (i + 1 < n) st.commit(kbuf + ((i + 1) & 1) * kBK * KS);
+              __syncthreads();
+            }
+          }
+          flush_bits();
+        }
+      }
+      F0 += __shfl_xor(F0, 32);
+      F1 += __shfl_xor(F1, 32);
+      F2 += __shfl_xor(F2, 32);
+      tau_step<AK>(F0, F1, F2, P.beta, P.mode, P.tol, max_iters, lo, hi, tau, conv, iters);
+      // Candidates of the next sweep: tau only moves up from lo, so a tile with
+      // no score above the lo this sweep used stays empty for every row; a wave
+      // whose rows have all converged needs none.  (Only this wave's bits are
+      // written; every reader of them passed a barrier since its last read.)
+      if (wave_busy && !dense) {
+        const bool busy_next = __ballot(!conv) != 0ull;
+        for (int e = lane; e < n_words; e += kWave) cbits[w * n_words + e] = busy_next ? lbits[w * n_words + e] : 0u;
+      }
+    }
+
+    // block_mask row of this wave from the final bits (every tile, so no zero fill)
+    if (wave_rows) {
+      for (int kt = lane; kt < P.n_kt; kt += kWave) {
+        const uint32_t b = 1u << (kt & 31), e = (uint32_t)(kt >> 5);
+        const bool m = mbits[w * n_words + e] & b;
+        const uint32_t v = m ? (1u | ((hbits[w * n_words + e] & b) ? 2u : 0u) |
+                                ((hbits[(kWaves + w) * n_words + e] & b) ? 4u : 0u))
+                             : 0u;
+        mrow[kt] = (uint8_t)v;
+      }
+    }
+    if (valid && h == 0) {
+      tau_out[(size_t)bh * P.ld + iq] = tau;
+      if (iters_out) iters_out[(size_t)bh * P.ld + iq] = (uint8_t)min(iters, 255);
+    }
+
+    // ---- P V over the active tiles of the final mask (bf16).  Q is still in
+    // registers, tau in a register and the mask in LDS; V tiles take the
+    // histogram's place.
+    if constexpr (kFusePV) {
+      __syncthreads();   // every wave's final mask bits (and the histogram is dead)
+      char* vbuf = reinterpret_cast<char*>(hist);                       // 2 x [64][KS]
+      const E* Vh = V + (size_t)bh * P.ld * D;
+      const float ptau = valid ? tau : INFINITY;
+      f32x16 oacc[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+      auto active = [&](int ww, int kt) -> bool { return (mbits[ww * n_words + (kt >> 5)] >> (kt & 31)) & 1u; };
+      RowTiles<E, D, kBK> sk(Kh, N, w, lane), sv(Vh, N, w, lane);
+      for (int base = 0; base < kt_end; base += kChunk) {
+        const int n = build_list(base, min(kChunk, kt_end - base), active, list, wbits, flags, counter);
+        if (n > 0) {
+          sk.fetch(kbuf, (base + list[0]) * kBK);
+          sv.fetch(vbuf, (base + list[0]) * kBK);
+          sk.commit(kbuf);
+          sv.commit(vbuf);
+        }
+        __syncthreads();
+        for (int i = 0; i < n; ++i) {
+          const int kt = base + list[i];
+          const int nb = (i + 1) & 1;
+          if (i + 1 < n) {
+            sk.fetch(kbuf + nb * kBK * KS, (base + list[i + 1]) * kBK);
+            sv.fetch(vbuf + nb * kBK * KS, (base + list[i + 1]) * kBK);
+          }
+          if ((wbits[i] >> w) & 1) {
+            const char* kl = kbuf + (i & 1) * kBK * KS;
+            const char* vl = vbuf + (i & 1) * kBK * KS;
+            const int lim = row_limit(kt * kBK, iq, N, P.causal, h);
+            if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
+              pv_tile<E, D, AK, true>(oacc, kl, vl, KS, qf, lane, lim, ptau, P);
+            else
+              pv_tile<E, D, AK, false>(oacc, kl, vl, KS, qf, lane, lim, ptau, P);
+          }
+          if (i + 1 < n) {
+            sk.commit(kbuf + nb * kBK * KS);
+            sv.commit(vbuf + nb * kBK * KS);
+          }
+          __syncthreads();
+        }
+      }
+      if (valid) store_out<D>(oacc, out, (size_t)bh * P.ld + iq, h, P.out_bf16 != 0);
+    }
+  };
+  if constexpr (kFusePV) {
+    // persistent (bf16): one workgroup per resident slot, units from the work queue
+    __shared__ int s_unit;
+    int bh, qtile;
+    while (next_unit(queue, &s_unit, (N + kBQW - 1) / kBQW, P.BH, P.causal, bh, qtile)) {
+      unit(bh, qtile);
+      __syncthreads();   // the next unit reuses the LDS
+    }
+  } else {
+    int bh, qtile;
+    map_tile((N + kBQW - 1) / kBQW, P.BH, P.causal, bh, qtile);
+    unit(bh, qtile);
   }
 }
 
@@ -2744,9 +2839,9 @@ size_t maskt_bytes(const Shape& s) {
 }
 
 size_t workspace_bytes(const Shape& s) {
-  // forward: [V^T] | row maxima | block codes;
+  // forward: [V^T] | row maxima | block codes | work queues;
   // backward: [K^T | Q^T | dO^T] | delta | transposed mask
-  const size_t fwd = transposed_bytes(s) + row_bytes(s) + blkcode_bytes(s);
+  const size_t fwd = transposed_bytes(s) + row_bytes(s) + blkcode_bytes(s) + kQueueBytes;
   const size_t bwd = 3 * transposed_bytes(s) + row_bytes(s) + maskt_bytes(s);
   const size_t ws = bwd > fwd ? bwd : fwd;
   return ws > 256 ? ws : 256;
@@ -2809,6 +2904,22 @@ bool pair_query_tiles(const Shape& s, int causal) {
   return 2 * tiles > 3 * slots && 2 * tiles <= 5 * slots;
 }
 
+// Workgroups of a persistent kernel (next_unit): as many as stay resident at
+// once (the occupancy for its LDS size, times the compute units), at most
+// one per unit; a multiple of 8 when there is one queue per XCD, so that
+// every queue has workgroups on its XCD.
+int persistent_grid(const void* fn, size_t lds, int units, int BH) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0 ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds) != hipSuccess || per_cu <= 0)
+    per_cu = 1, cus = 64;
+  int g = cus * per_cu;
+  if (g > units) g = units;
+  if ((BH & 7) == 0) g = (g + 7) & ~7;   // units is then a multiple of 8 too
+  return g > 0 ? g : 1;
+}
+
 // Records the caller's timing events around one stage (no-op without events).
 struct StageTimer {
   void* const* ev;
@@ -2859,6 +2970,7 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
   E* Vt = reinterpret_cast<E*>(w);
   float* rowmax = reinterpret_cast<float*>(w + transposed_bytes(s));
   uint8_t* blkc = reinterpret_cast<uint8_t*>(w + transposed_bytes(s) + row_bytes(s));
+  int* queue = reinterpret_cast<int*>(w + transposed_bytes(s) + row_bytes(s) + blkcode_bytes(s));
 
   // every LDS size is checked and allowed before anything is enqueued
   const size_t rm_lds = kTr ? (size_t)2 * kRowmaxTPS * DirectTile<D>::BYTES : (size_t)2 * kBK * KS;
@@ -2889,17 +3001,22 @@ int launch_fwd(const Shape& s, Params P, const void* q, const void* k, const voi
     P.pair_qt = pair_query_tiles(s, P.causal) ? 1 : 0;
     const int n_qt = (s.N + kRowmaxQ - 1) / kRowmaxQ;
     const int units = P.pair_qt ? (n_qt + 1) / 2 : n_qt;
-    rc = launch(k_rowmax16<D>, dim3(units * s.BH), dim3(64 * kRowmaxWaves), rm_lds, st, Q, K, P, rowmax, blkc);
+    rc = launch(k_rowmax16<D>, dim3(units * s.BH), dim3(64 * kRowmaxWaves), rm_lds, st, Q, K, P, rowmax, blkc,
+                queue);
   } else {
-    rc = launch(k_rowmax<E, D>, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, blkc);
+    rc = launch(k_rowmax<E, D>, dim3(s.n_qt256 * s.BH), dim3(kThreads), rm_lds, st, Q, K, P, rowmax, blkc,
+                queue);
   }
   if (rc != EA_OK) return rc;
   tm.end(EA_STAGE_ROWMAX);
 
   const dim3 g(s.n_qt128 * s.BH);
   tm.begin(EA_STAGE_TAU);   // bf16: tau, block mask and P V in one kernel
-  if ((rc = launch(ktau, g, dim3(kThreads), tau_lds, st, Q, K, V, (const float*)rowmax, (const uint8_t*)blkc, P,
-                   tau, mask, iters, out)) != EA_OK)
+  // bf16: persistent workgroups (next_unit)
+  const dim3 gp(kTr ? persistent_grid(reinterpret_cast<const void*>(ktau), tau_lds, s.n_qt128 * s.BH, s.BH)
+                    : s.n_qt128 * s.BH);
+  if ((rc = launch(ktau, gp, dim3(kThreads), tau_lds, st, Q, K, V, (const float*)rowmax, (const uint8_t*)blkc, P,
+                   tau, mask, iters, out, queue)) != EA_OK)
     return rc;
   tm.end(EA_STAGE_TAU);
 
@@ -3030,8 +3147,10 @@ int static_scratch(void** out) {
   return EA_OK;
 }
 
-// forward part of the workspace: [V^T] | row maxima | block codes
-size_t fwd_workspace_bytes(const Shape& s) { return transposed_bytes(s) + row_bytes(s) + blkcode_bytes(s); }
+// forward part of the workspace: [V^T] | row maxima | block codes | work queues
+size_t fwd_workspace_bytes(const Shape& s) {
+  return transposed_bytes(s) + row_bytes(s) + blkcode_bytes(s) + kQueueBytes;
+}
 
 #define EA_DISPATCH(FN, ...)                                                          \
   do {                                                                                \

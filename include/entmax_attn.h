@@ -114,7 +114,8 @@ typedef struct {
  * tiles -- the size of the block mask, B*H*ceil(N/32)*ceil(N/64) bytes, never
  * a score matrix (the fused kernel's memory grows like its inputs and its
  * block mask: "AdaSplash: Adaptive Sparse Flash Attention", "AdaSplash: Fused
- * GPU Kernel for Attention"); (backward) the block mask transposed; and for
+ * GPU Kernel for Attention"); 256 bytes of work-queue counters (forward;
+ * the call sets them itself); (backward) the block mask transposed; and for
  * fp32 inputs transposed copies of V (forward) or of K, Q, dO (backward).
  * Returns 0 for an invalid desc. */
 size_t entmax_attn_workspace_bytes(const ea_desc* desc);

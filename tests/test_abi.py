@@ -72,25 +72,26 @@ def _align(x):
 
 def test_workspace_is_rows_plus_mask_sized_codes():
     """Workspace = one float per row + one byte per (32-query block, 64-key
-    tile), rows padded to 64 tiles (the size of the block mask), + the
-    transposed copies for fp32 inputs.  It grows like the block mask (about
-    N^2 / 2048 bytes per head), never like a score matrix."""
+    tile), rows padded to 64 tiles (the size of the block mask), + 256 bytes
+    of work-queue counters, + the transposed copies for fp32 inputs.  It grows
+    like the block mask (about N^2 / 2048 bytes per head), never like a score
+    matrix."""
     for n in (1000, 4096, 16384, 131072):
         bh = 16
         nk, nq = -(-n // 64), -(-n // 32)
         d = A.make_desc(1, bh, n, 128)
         ws = A.entmax_attn_workspace_bytes(d)
         codes = _align(bh * nq * (-(-nk // 64) * 64))
-        assert ws == _align(bh * n * 4) + codes
-        assert ws <= bh * n * 4 + bh * nq * (nk + 63) + 512
+        assert ws == _align(bh * n * 4) + codes + 256
+        assert ws <= bh * n * 4 + bh * nq * (nk + 63) + 1024
         f = A.make_desc(1, bh, n, 128, in_dtype=0)
         tr = _align(bh * 128 * nk * 64 * 4)
         mt = _align(bh * nk * ((nq + 3) // 4 * 4))      # transposed block mask
         assert A.entmax_attn_workspace_bytes(f) == max(tr + ws, 3 * tr + _align(bh * n * 4) + mt)
     # the largest accepted length: one head at N = 2^20 needs the 512 MiB of
-    # its block mask plus 4 MiB of row maxima
+    # its block mask plus 4 MiB of row maxima (and the queue counters)
     big = A.entmax_attn_workspace_bytes(A.make_desc(1, 1, 1 << 20, 128))
-    assert big == (1 << 22) + (1 << 15) * (1 << 14)
+    assert big == (1 << 22) + (1 << 15) * (1 << 14) + 256
     d = A.make_desc(2, 3, 1000, 64, out_dtype=1)
     assert A.entmax_attn_mask_dims(d) == (32, 16, 32, 64)
 
