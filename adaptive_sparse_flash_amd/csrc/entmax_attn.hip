@@ -1152,8 +1152,8 @@ __device__ __forceinline__ float model_pow(float z, float beta, float& deriv) {
 // "Sparse Attention Makes Waves"); the bin count, the moments and the
 // two-point start model are this library's.
 //
-// hist_add takes yc = y clamped to [0, 1] (0 drops the entry) and the LDS
-// address of the row's histogram.  With 0 < yc <= 1 and ysc = 2^S - 1
+// hist_add takes yc = y clamped to [0, 1] (entries at or below ylim >= 0 are
+// dropped) and the LDS address of the row's histogram.  With 0 < yc <= 1 and ysc = 2^S - 1
 // (S <= 24) the product rounds to at most 2^S - 1, so Y needs no clamp and
 // Y^2 comes from the two 24-bit multiplies.  kAsm issues the two atomics by
 // inline assembly: the compiler cannot tell the histogram from the tiles
@@ -1163,8 +1163,8 @@ __device__ __forceinline__ float model_pow(float z, float beta, float& deriv) {
 // before the histogram is read.)
 template <bool kAsm>
 __device__ __forceinline__ void hist_add(uint32_t hrow, unsigned long long* hr, float yc, float bin_scale,
-                                         float ysc, int bins) {
-  if (yc > 0.0f) {
+                                         float ysc, int bins, float ylim = 0.0f) {
+  if (yc > ylim) {
     const unsigned Y = (unsigned)(yc * ysc);
     __builtin_assume(Y < (1u << 24));
     const int b = min((int)(yc * bin_scale), bins - 1);
@@ -1625,8 +1625,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
         // above its own raised bound (less a rounding margin), kept in mbits.
         // The block codes test a 32-row block against its loosest row; these
         // bits test every row against its own bound, and tau's bin only lies
-        // higher, so they prune the first refinement sweep's candidates.
+        // higher, so they prune the first refinement sweep's candidates.  And
+        // pass 2 bins only the scores above that bound: the edges below it
+        // are never read (f at the bound is already >= 0), and every score in
+        // a bin at or above it passes.
         const float gy = valid ? (lo - lo0) - 4.0f * FLT_EPSILON * (fmaxf(1.0f, fabsf(xmax)) + 2.0f) : 2.0f;
+        const float ylim = hp == 2 ? fmaxf(gy, 0.0f) : 0.0f;   // (yc = 0 stays dropped)
         int bit_wd = -1;
         uint32_t r_word = 0u;
         auto flush_row_bits = [&]() {
@@ -1660,7 +1664,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
                   for (int j = 0; j < 16; ++j) {
                     const float yc = clamp01(fmaf(acc[kb][j], P.scale, -lo0));
                     ymax = fmaxf(ymax, yc);
-                    hist_add<true>(hrow, hr, yc, bin_scale, ysc, BINS);
+                    hist_add<true>(hrow, hr, yc, bin_scale, ysc, BINS, ylim);
                   }
               };
               if (wave_has_tail || (kt * kBK + kBK > N) || (P.causal && kt * kBK + kBK - 1 > wq0))
