@@ -640,15 +640,19 @@ struct ColStage {
 template <int BITS = 1, typename Pred>
 __device__ __forceinline__ int build_list(int base, int len, Pred pred, short* list, uint8_t* wbits,
                                           uint8_t* flags, int* counter) {
-  for (int i = threadIdx.x; i < len; i += kThreads) {
+  // (the thread index through an empty asm statement: in a persistent
+  // kernel's unit loop nothing derived from it is kept live across units)
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  for (int i = tid; i < len; i += kThreads) {
     uint32_t b = 0;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) b |= ((uint32_t)pred(ww, base + i) & ((1u << BITS) - 1u)) << (BITS * ww);
     flags[i] = (uint8_t)b;
   }
   __syncthreads();
-  if (threadIdx.x < kWave) {
-    const int lane = threadIdx.x;
+  if (tid < kWave) {
+    const int lane = tid;
     int count = 0;
     for (int b0 = 0; b0 < len; b0 += kWave) {
       const int i = b0 + lane;
@@ -1439,7 +1443,7 @@ template <typename E, int D, int AK, int BINS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(E) == 2 ? 2 : 1, 2))) void k_tau(const E* __restrict__ Q, const E* __restrict__ K,
                                                   const E* __restrict__ V,
                                                   const float* __restrict__ rowmax,
-                                                  const uint8_t* __restrict__ blkc, Params P,
+                                                  const uint8_t* __restrict__ blkc, Params Pk,
                                                   float* __restrict__ tau_out,
                                                   uint8_t* __restrict__ mask_out,
                                                   uint8_t* __restrict__ iters_out,
@@ -1447,7 +1451,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int KS = row_stride<E, D>();
   constexpr bool kFusePV = sizeof(E) == 2;   // bf16: P V runs here, after tau
-  const int N = P.N;
+  const int N = Pk.N;
   // one work unit: query tile qtile of head bh
   auto unit = [&](const int bh, const int qtile) {
     // The thread index passes through an empty asm statement, so that nothing
@@ -1456,6 +1460,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     int tid = (int)threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, w = tid >> 6, h = lane >> 5, c32 = lane & 31;
+    // Likewise the parameters that feed double-precision set-up (the
+    // histogram's fixed-point unit, the bracket, the Halley step): with
+    // both, the kernel fits two waves per SIMD without spills.
+    Params P = Pk;
+    asm volatile("" : "+s"(P.alpha), "+s"(P.beta), "+s"(P.scale), "+s"(P.tol), "+s"(P.hshift));
     const int q0 = qtile * kBQW;
     const int wq0 = q0 + kBQ * w;
     const int iq = wq0 + c32;
@@ -1577,7 +1586,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
 
     // ---- histogram initialisation (AdaSplash-2)
     if (P.mode == EA_TAU_HIST_HALLEY) {
-      for (int e = threadIdx.x; e < kBQW * HROW; e += kThreads) hist[e] = 0ull;
+      for (int e = tid; e < kBQW * HROW; e += kThreads) hist[e] = 0ull;
       unsigned long long* hr = hist + (size_t)(kBQ * w + c32) * HROW;
       // Bins split [lo, hi]; moments are kept in units of 1/(2^S - 1) of y = x - lo <= 1
       // with Y <= 2^S - 1: the count sits at bit 40, sum Y below it and sum Y^2
@@ -1605,7 +1614,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
       const bool two = strong_pass && weak_lanes > kStrongMinWeak;
       if (two) {
         // the union of the waves' strong tiles, in lbits (first written by the sweeps)
-        for (int e = threadIdx.x; e < n_words; e += kThreads)
+        for (int e = tid; e < n_words; e += kThreads)
           lbits[e] = mbits[e] | mbits[n_words + e] | mbits[2 * n_words + e] | mbits[3 * n_words + e];
         __syncthreads();
       }
@@ -1948,13 +1957,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof
     // persistent (bf16): one workgroup per resident slot, units from the work queue
     __shared__ int s_unit;
     int bh, qtile;
-    while (next_unit(queue, &s_unit, (N + kBQW - 1) / kBQW, P.BH, P.causal, bh, qtile)) {
+    while (next_unit(queue, &s_unit, (N + kBQW - 1) / kBQW, Pk.BH, Pk.causal, bh, qtile)) {
       unit(bh, qtile);
       __syncthreads();   // the next unit reuses the LDS
     }
   } else {
     int bh, qtile;
-    map_tile((N + kBQW - 1) / kBQW, P.BH, P.causal, bh, qtile);
+    map_tile((N + kBQW - 1) / kBQW, Pk.BH, Pk.causal, bh, qtile);
     unit(bh, qtile);
   }
 }
