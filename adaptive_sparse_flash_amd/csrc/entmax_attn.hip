@@ -37,7 +37,12 @@
 //  * The histogram holds integer moments (count, sum y, sum y^2 of
 //    y = x - lo in fixed point, Y = floor(y (2^S - 1)) with S chosen from N)
 //    updated with LDS integer atomics, so it is deterministic and, for alpha
-//    in {1.5, 2}, gives f exactly at bin edges.
+//    in {1.5, 2}, gives f exactly at bin edges.  There it is built in two
+//    passes: the strong tiles first, whose partial moments bound tau from
+//    below and prune the rest, then the remaining candidates of that bound.
+//  * The bf16 tau kernel is persistent: one workgroup per resident slot
+//    takes heavy-first query tiles from per-XCD work queues, which keeps the
+//    slots busy where the hardware dispatcher would hold workgroups back.
 //  * The sparse kernels stage d = 128 bf16 tiles with buffer_load ... lds
 //    (no staging registers) and keep LDS reads several MFMA steps ahead.
 //  * For bf16 the tau kernel ends with the P V pass over its final mask
